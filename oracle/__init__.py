@@ -1,0 +1,187 @@
+"""The CPU oracle for C = epilogue(A . B) -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product (``tensor_core_gemm_amd``)
+never imports it, and it imports nothing from the product: the two share no
+code, header, table or constant.  Inputs cross over as raw 16-bit patterns
+(numpy ``uint16`` arrays), produced by the seeded generators in
+``gemm_workloads``.
+
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc and OpenMP,
+``-ffp-contract=off``).  It follows the worked example of the page
+"gizml:tile": a zero accumulator (Program.zeros), a fold over k in ascending
+order (Program.fold), products and sums in F32 (Tile.dot), max(x, 0)
+(Tile.relu, with Tile.maximum's NaN rule), then rounding to the storage type
+(Tile.to).  Storage codes are the page's constants: F32 = 0, F16 = 4,
+BF16 = 5.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+F32, F16, BF16 = 0, 4, 5
+EPI_NONE, EPI_RELU = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no GPU code involved)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+               "-shared", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            lib.oracle_decode.argtypes = [_int, _vp, _vp, _i64]
+            lib.oracle_decode.restype = None
+            lib.oracle_encode.argtypes = [_int, _vp, _vp, _i64]
+            lib.oracle_encode.restype = None
+            lib.oracle_max_threads.argtypes = []
+            lib.oracle_max_threads.restype = _int
+            lib.oracle_gemm.argtypes = [_i64, _i64, _i64, _int, _int, _int, _i64, _vp, _i64, _vp,
+                                        _i64, _vp, _i64, _vp, _int]
+            lib.oracle_gemm.restype = _int
+            lib.oracle_gemm_sampled.argtypes = [_i64, _i64, _i64, _int, _int, _int, _i64, _vp,
+                                                _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
+                                                _int]
+            lib.oracle_gemm_sampled.restype = _int
+            lib.oracle_gemm_f64.argtypes = [_i64, _i64, _i64, _int, _i64, _vp, _i64, _vp, _i64,
+                                            _vp, _vp, _int]
+            lib.oracle_gemm_f64.restype = _int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_vp)
+
+
+def _bits(x) -> np.ndarray:
+    """Raw 16-bit patterns as a C-contiguous uint16 numpy array."""
+    if hasattr(x, "detach"):  # a torch tensor of dtype float16/bfloat16/int16
+        import torch  # local: the oracle itself needs no torch
+
+        t = x.detach().cpu().contiguous()
+        if t.dtype in (torch.float16, torch.bfloat16):
+            t = t.view(torch.int16)
+        x = t.numpy()
+    a = np.ascontiguousarray(x)
+    if a.dtype != np.uint16:
+        a = a.view(np.uint16) if a.dtype.itemsize == 2 else None
+    if a is None:
+        raise TypeError("expected 16-bit patterns")
+    return a
+
+
+def threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def decode(dtype: int, bits) -> np.ndarray:
+    b = _bits(bits)
+    out = np.empty(b.shape, np.float32)
+    _load().oracle_decode(dtype, _ptr(b), _ptr(out), b.size)
+    return out
+
+
+def encode(dtype: int, values) -> np.ndarray:
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_encode(dtype, _ptr(v), _ptr(out), v.size)
+    return out
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise ValueError({-1: "bad argument", -2: "bad dtype", -3: "out of memory"}.get(rc, rc))
+
+
+def gemm(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, epilogue: int,
+         batch: int = 1, stride_a: int | None = None, stride_b: int | None = None,
+         want_y: bool = False, n_threads: int = 0):
+    """C = epilogue(A . B) for [batch][M][K] x [batch][K][N] row-major operands.
+
+    Returns C as float32 (out F32) or uint16 patterns (F16/BF16), shape
+    [batch, M, N], and, if ``want_y``, the fp32 value before rounding too.
+    """
+    a, b = _bits(A).reshape(-1), _bits(B).reshape(-1)
+    sa = M * K if stride_a is None else stride_a
+    sb = K * N if stride_b is None else stride_b
+    if batch < 1 or a.size < (batch - 1) * sa + M * K or b.size < (batch - 1) * sb + K * N:
+        raise ValueError("operand arrays smaller than the shape and strides need")
+    C = np.zeros((batch, M, N), np.float32 if out_dtype == F32 else np.uint16)
+    Y = np.zeros((batch, M, N), np.float32) if want_y else None
+    _check(_load().oracle_gemm(M, N, K, in_dtype, out_dtype, epilogue, batch, _ptr(a), sa,
+                               _ptr(b), sb, _ptr(C), M * N, _ptr(Y) if Y is not None else None,
+                               n_threads))
+    return (C, Y) if want_y else C
+
+
+def gemm_sampled(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, epilogue: int,
+                 bi, ii, jj, batch: int = 1, stride_a: int | None = None,
+                 stride_b: int | None = None, n_threads: int = 0):
+    """The oracle for the listed elements C[bi[e], ii[e], jj[e]] only.
+
+    Returns (values in out_dtype storage, fp32 y before rounding).
+    """
+    a, b = _bits(A).reshape(-1), _bits(B).reshape(-1)
+    sa = M * K if stride_a is None else stride_a
+    sb = K * N if stride_b is None else stride_b
+    bi = np.ascontiguousarray(bi, np.int64)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    if not (bi.shape == ii.shape == jj.shape):
+        raise ValueError("index arrays differ in shape")
+    if a.size < (batch - 1) * sa + M * K or b.size < (batch - 1) * sb + K * N:
+        raise ValueError("operand arrays smaller than the shape and strides need")
+    out = np.zeros(ii.shape, np.float32 if out_dtype == F32 else np.uint16)
+    Y = np.zeros(ii.shape, np.float32)
+    _check(_load().oracle_gemm_sampled(M, N, K, in_dtype, out_dtype, epilogue, batch, _ptr(a),
+                                       sa, _ptr(b), sb, ii.size, _ptr(bi), _ptr(ii), _ptr(jj),
+                                       _ptr(out), _ptr(Y), n_threads))
+    return out, Y
+
+
+def gemm_f64(A, B, M: int, N: int, K: int, in_dtype: int, batch: int = 1,
+             stride_a: int | None = None, stride_b: int | None = None, n_threads: int = 0):
+    """fp64 twin: (sum in double before any epilogue, sum of |a||b|)."""
+    a, b = _bits(A).reshape(-1), _bits(B).reshape(-1)
+    sa = M * K if stride_a is None else stride_a
+    sb = K * N if stride_b is None else stride_b
+    if a.size < (batch - 1) * sa + M * K or b.size < (batch - 1) * sb + K * N:
+        raise ValueError("operand arrays smaller than the shape and strides need")
+    Y = np.zeros((batch, M, N), np.float64)
+    S = np.zeros((batch, M, N), np.float64)
+    _check(_load().oracle_gemm_f64(M, N, K, in_dtype, batch, _ptr(a), sa, _ptr(b), sb, _ptr(Y),
+                                   _ptr(S), n_threads))
+    return Y, S
+
+
+def to_float(dtype: int, C) -> np.ndarray:
+    """Output storage -> float32 values (identity for F32)."""
+    C = np.asarray(C)
+    return C.astype(np.float32) if dtype == F32 else decode(dtype, C)
