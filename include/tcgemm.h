@@ -1,0 +1,172 @@
+/*
+ * tcgemm.h -- C ABI of libtcgemm.so: C = epilogue(A . B) on an AMD Instinct
+ * MI355X (gfx950), with operand tiles staged through LDS before the MFMA
+ * units read their fragments.
+ *
+ * What one run computes, for every batch item b, row i < M, column j < N
+ * (page "gizml:tile": the worked example, Program.zeros, Program.fold,
+ * Tile.dot, Tile.relu, Tile.to, In.at, Out.put):
+ *
+ *     acc = +0, then acc += A[b,i,k] * B[b,k,j] for k = 0 .. K-1, in fp32
+ *     y   = relu ? (acc > 0 ? acc : +0) : acc
+ *     C[b,i,j] = y rounded to nearest-even in the output storage type
+ *
+ * Elements outside the matrices read as 0 (In.at) and elements outside C are
+ * never written (Out.put: "the rest keeps its values").  The staged kernel
+ * and the unstaged kernel of the same plan perform the same MFMA sequence on
+ * the same values, so they return the same bits (page "Module Tolk.Stage":
+ * staging moves values and never rounds them).
+ *
+ * Layout: A is [batch][M][K], B is [batch][K][N], C is [batch][M][N], all
+ * row-major with contiguous rows (row pitch K, N and N elements).  stride_*
+ * is the distance in elements between consecutive batch items (ignored when
+ * batch == 1).  Storage codes are the page's constants (F32 = 0, F16 = 4,
+ * BF16 = 5); A and B share one input type ("operands of one type", Tile.dot).
+ *
+ * Threading: plans are immutable after creation and may be used from any
+ * thread and on any stream.  gemm_run allocates nothing, never
+ * synchronises, and is asynchronous with respect to the host.
+ *
+ * Errors: every int-returning call returns GEMM_OK (0) or a negative
+ * GEMM_E_* code; gemm_strerror names it.  (Named, specific failures follow
+ * the error convention of the page "Module Tolk.Uniform", check.)
+ */
+#ifndef TCGEMM_H
+#define TCGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage codes (page "gizml:tile", Constants). */
+enum { GEMM_F32 = 0, GEMM_F16 = 4, GEMM_BF16 = 5 };
+
+/* Epilogues: none, or max(y, 0) with NaN and -0 giving +0 (Tile.relu). */
+enum { GEMM_EPI_NONE = 0, GEMM_EPI_RELU = 1 };
+
+/* Plan flags.
+ *   GEMM_FLAG_FORCE_STAGES_1: use at most one LDS stage even where two fit.
+ *   GEMM_FLAG_UNSTAGED: no LDS staging; fragments are loaded straight from
+ *     global memory (the "Setting.stage off" case of the page "Module
+ *     Tolk.Stage", depth). */
+enum { GEMM_FLAG_FORCE_STAGES_1 = 1, GEMM_FLAG_UNSTAGED = 2 };
+
+/* Error codes. */
+enum {
+  GEMM_OK = 0,
+  GEMM_E_ARG = -1,     /* bad size, stride, flag, tile id or null pointer      */
+  GEMM_E_DTYPE = -2,   /* unsupported input/output storage type                */
+  GEMM_E_ALIGN = -3,   /* a pointer is not aligned to its element size         */
+  GEMM_E_ALIAS = -4,   /* C overlaps A or B (page "Module Tolk.Uniform":
+                          parameters that are written may not overlap others) */
+  GEMM_E_DEVICE = -5,  /* no usable gfx950 device, or the plan does not fit it */
+  GEMM_E_LAUNCH = -6,  /* the kernel launch failed (hipGetLastError)           */
+  GEMM_E_NOMEM = -7,   /* host allocation of the plan failed                   */
+  GEMM_E_PLAN = -8,    /* null or destroyed plan                               */
+  GEMM_E_SIZE = -9     /* a tile's byte offsets would not fit 31 bits          */
+};
+
+/* The problem.  M, N >= 0, K >= 0 (K == 0 gives C = epilogue(+0));
+ * batch >= 1; with batch > 1, stride_a >= M*K, stride_b >= K*N and
+ * stride_c >= M*N.  `tile` selects a tile configuration by id (1 ..
+ * gemm_tile_count()), or 0 for the planner's choice. */
+typedef struct gemm_desc {
+  int64_t M, N, K;
+  int32_t in_dtype;  /* GEMM_F16 or GEMM_BF16 (A and B)      */
+  int32_t out_dtype; /* GEMM_F32, GEMM_F16 or GEMM_BF16 (C)   */
+  int32_t epilogue;  /* GEMM_EPI_NONE or GEMM_EPI_RELU         */
+  int32_t flags;     /* GEMM_FLAG_* bits                       */
+  int64_t batch;
+  int64_t stride_a, stride_b, stride_c;
+  int32_t tile;
+  int32_t reserved; /* must be 0 */
+} gemm_desc;
+
+/* What the planner needs to know about a device (page "Module Tolk.Stage":
+ * Renderer.t.async_copy and Renderer.t.shared_max). */
+typedef struct gemm_device_caps {
+  int32_t num_cus;    /* compute units                                   */
+  int32_t lds_bytes;  /* LDS one workgroup may hold (163840 on gfx950)   */
+  int32_t async_copy; /* 1: global->LDS copies overlap compute            */
+  int32_t wave_size;  /* 64                                               */
+  int32_t clock_khz;  /* peak engine clock                                */
+  int32_t num_xcds;   /* accelerator complex dies sharing the dispatch    */
+  char arch[64];      /* e.g. "gfx950:sramecc+:xnack-"                     */
+} gemm_device_caps;
+
+/* A plan's decisions, for tests and reports. */
+typedef struct gemm_plan_info {
+  int32_t tile_id;
+  int32_t bm, bn, bk;       /* workgroup tile                                */
+  int32_t waves;            /* waves (64 lanes) per workgroup                */
+  int32_t stages;           /* 2, 1, or 0 (unstaged)                         */
+  int32_t lds_bytes;        /* LDS the kernel declares                       */
+  int32_t vec16;            /* 1: 16-byte copies; 0: element copies          */
+  int64_t tiles_m, tiles_n; /* output tiles along M and N                    */
+  int64_t workgroups;       /* tiles_m * tiles_n * batch                     */
+  int64_t trips;            /* K-trips: ceil(K / bk)                         */
+  int64_t mfma_per_run;     /* MFMA instructions one run issues              */
+  int32_t mfma_m, mfma_n, mfma_k;
+  int32_t reserved;
+} gemm_plan_info;
+
+typedef struct gemm_plan_s* gemm_plan_t;
+
+/* Device capabilities of HIP device `device` (host call; no kernel). */
+int gemm_device_caps_query(int device, gemm_device_caps* out);
+
+/* Plan for the current HIP device (queries it once per device). */
+int gemm_plan(const gemm_desc* desc, gemm_plan_t* out);
+
+/* Plan for the given capabilities: host only, no device needed. */
+int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps* caps, gemm_plan_t* out);
+
+/* Copy a plan's decisions out. */
+int gemm_plan_get_info(gemm_plan_t plan, gemm_plan_info* out);
+
+/* A one-line description (tile, stages, LDS bytes, grid, MFMA shape); the
+ * string belongs to the plan. */
+const char* gemm_plan_describe(gemm_plan_t plan);
+
+/*
+ * Launch C = epilogue(A . B) on `stream` (a hipStream_t; NULL = the null
+ * stream).  A, B, C are device pointers owned by the caller, aligned to
+ * their element size; 16-byte-aligned A and B with K and N multiples of 8
+ * take the 16-byte copy path, others take the element path (same bits).
+ * Only C's M x N region of each batch item is written.  Returns
+ * GEMM_E_ALIAS if C's extent overlaps A's or B's, GEMM_E_DEVICE if the
+ * current device is not gfx950 or holds less LDS than the plan needs, and
+ * GEMM_E_LAUNCH if the launch fails.  M == 0 or N == 0 launches nothing.
+ */
+int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream);
+
+/* Free a plan (NULL is ignored). */
+void gemm_plan_destroy(gemm_plan_t plan);
+
+/* Static text naming an error code. */
+const char* gemm_strerror(int code);
+
+/*
+ * The stage-count rule (page "Module Tolk.Stage", depth): with operand tiles
+ * of tile_bytes[0 .. n_tiles-1] bytes each and `used` bytes of LDS taken by
+ * others, 2 where caps->async_copy and two stages fit caps->lds_bytes, 1
+ * where one does, and 0 where neither does, where n_tiles == 0, where a tile
+ * holds less than one 16-byte copy, where the device has no LDS or no
+ * lanes, or where stage_enabled == 0.
+ */
+int gemm_stage_depth(const gemm_device_caps* caps, int64_t used, const int64_t* tile_bytes,
+                     int n_tiles, int stage_enabled);
+
+/* Number of tile configurations (valid `tile` ids are 1 .. count). */
+int gemm_tile_count(void);
+
+/* HIP runtime version the library is running against (hipRuntimeGetVersion). */
+int gemm_runtime_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,76 @@
+/*
+ * tcgemm_probe.h -- diagnostic kernels that pin the gfx950 lane layouts the
+ * GEMM kernels rely on.  They are part of libtcgemm.so but not of the GEMM
+ * path; the tests call them to check, on the hardware, the assumptions the
+ * fragment loaders make.
+ *
+ * All pointers named *_dev are device memory owned by the caller; *_host
+ * arguments are host memory read before the call returns.  Every function
+ * launches one workgroup on `stream` (a hipStream_t, or NULL for the null
+ * stream), returns 0 on success or a negative GEMM_E_* code (tcgemm.h), and
+ * does not synchronise.  Host-side checks reject any address that would fall
+ * outside the probe's LDS buffer, so every probe stays in bounds.
+ *
+ * Why these exist: the page "Module Tolk.Stage" has the cores read their
+ * fragments back from the staged (swizzled) tile, and the TVM page on
+ * ldmatrix/stmatrix lowering describes fragment loads as warp-collective
+ * 8x8 tile moves with a transposing form for the column-major side.  On
+ * gfx950 the matching tools are the MFMA operand layouts, the transposing
+ * LDS read ds_read_b64_tr_b16 and the buffer load that writes LDS directly;
+ * their lane mappings are measured here instead of assumed.
+ */
+#ifndef TCGEMM_PROBE_H
+#define TCGEMM_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* MFMA shapes a probe can run. */
+enum {
+  TCG_PROBE_MFMA_32x32x16_BF16 = 0,
+  TCG_PROBE_MFMA_32x32x16_F16 = 1,
+  TCG_PROBE_MFMA_16x16x32_BF16 = 2,
+  TCG_PROBE_MFMA_16x16x32_F16 = 3
+};
+
+/*
+ * One wave runs one MFMA with a zero accumulator.  a_regs_dev and b_regs_dev
+ * hold, per lane (64), the 8 16-bit operand values of that lane's source
+ * registers (lane-major: [64][8]); d_regs_dev receives per lane the 16 fp32
+ * result registers ([64][16]; the 16x16 shapes fill the first 4).
+ */
+int tcg_probe_mfma(int kind, const uint16_t* a_regs_dev, const uint16_t* b_regs_dev,
+                   float* d_regs_dev, void* stream);
+
+/*
+ * ds_read_b64_tr_b16: the LDS buffer (16 KiB) is filled from lds_init_dev
+ * (n_elems 16-bit values, n_elems <= 8192), then each lane of one wave
+ * issues the transposing read at its byte address lane_byte_addr_host[lane]
+ * (8-byte aligned, + 8 <= 16384).  out_dev receives the 4 16-bit values each
+ * lane gets back ([64][4]).
+ */
+int tcg_probe_ds_read_tr16(const uint16_t* lds_init_dev, int n_elems,
+                           const uint32_t* lane_byte_addr_host, uint16_t* out_dev, void* stream);
+
+/*
+ * Buffer load of 16 bytes per lane written straight to LDS.  The LDS buffer
+ * (8 KiB) is first filled with 0xDEADBEEF; then one wave loads from a buffer
+ * resource whose base is src_dev and whose size is num_records bytes, lane
+ * `l` at byte offset lane_voffset_host[l] (offsets >= num_records are out of
+ * range and must read 0; the caller keeps every offset + 16 within the
+ * memory src_dev really owns), with the LDS destination base lds_byte_base
+ * (16-byte aligned, + 1024 <= 8192).  The whole 8 KiB of LDS is then copied
+ * to out_dev (2048 words).
+ */
+int tcg_probe_buffer_lds(const uint32_t* src_dev, uint32_t num_records,
+                         const uint32_t* lane_voffset_host, uint32_t lds_byte_base,
+                         uint32_t* out_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

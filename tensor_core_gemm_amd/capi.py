@@ -1,0 +1,220 @@
+"""ctypes binding of include/tcgemm.h: the same entry points, marshalling only.
+
+Every computation happens in libtcgemm.so; this module converts Python
+values and torch tensors (device memory, streams) into the C arguments and
+turns negative return codes into GemmError.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+
+import torch
+
+from ._lib import lib
+
+F32, F16, BF16 = 0, 4, 5
+EPI_NONE, EPI_RELU = 0, 1
+FLAG_FORCE_STAGES_1, FLAG_UNSTAGED = 1, 2
+
+GEMM_OK = 0
+GEMM_E_ARG, GEMM_E_DTYPE, GEMM_E_ALIGN, GEMM_E_ALIAS = -1, -2, -3, -4
+GEMM_E_DEVICE, GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE = -5, -6, -7, -8, -9
+
+TORCH_TO_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+CODE_TO_TORCH = {v: k for k, v in TORCH_TO_CODE.items()}
+
+
+class gemm_desc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("epilogue", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("batch", ctypes.c_int64), ("stride_a", ctypes.c_int64),
+                ("stride_b", ctypes.c_int64), ("stride_c", ctypes.c_int64),
+                ("tile", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class gemm_device_caps(ctypes.Structure):
+    _fields_ = [("num_cus", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("async_copy", ctypes.c_int32), ("wave_size", ctypes.c_int32),
+                ("clock_khz", ctypes.c_int32), ("num_xcds", ctypes.c_int32),
+                ("arch", ctypes.c_char * 64)]
+
+
+class gemm_plan_info(ctypes.Structure):
+    _fields_ = [("tile_id", ctypes.c_int32), ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
+                ("bk", ctypes.c_int32), ("waves", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("vec16", ctypes.c_int32),
+                ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
+                ("workgroups", ctypes.c_int64), ("trips", ctypes.c_int64),
+                ("mfma_per_run", ctypes.c_int64), ("mfma_m", ctypes.c_int32),
+                ("mfma_n", ctypes.c_int32), ("mfma_k", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+_vp = ctypes.c_void_p
+_SIGS = {
+    "gemm_device_caps_query": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(gemm_device_caps)]),
+    "gemm_plan": (ctypes.c_int, [ctypes.POINTER(gemm_desc), ctypes.POINTER(_vp)]),
+    "gemm_plan_for_caps": (ctypes.c_int, [ctypes.POINTER(gemm_desc),
+                                          ctypes.POINTER(gemm_device_caps), ctypes.POINTER(_vp)]),
+    "gemm_plan_get_info": (ctypes.c_int, [_vp, ctypes.POINTER(gemm_plan_info)]),
+    "gemm_plan_describe": (ctypes.c_char_p, [_vp]),
+    "gemm_run": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
+    "gemm_plan_destroy": (None, [_vp]),
+    "gemm_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "gemm_stage_depth": (ctypes.c_int, [ctypes.POINTER(gemm_device_caps), ctypes.c_int64,
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int]),
+    "gemm_tile_count": (ctypes.c_int, []),
+    "gemm_runtime_version": (ctypes.c_int, []),
+}
+_fns = {}
+
+
+def _fn(name):
+    f = _fns.get(name)
+    if f is None:
+        f = getattr(lib(), name)
+        f.restype, f.argtypes = _SIGS[name]
+        _fns[name] = f
+    return f
+
+
+class GemmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {gemm_strerror(code)} (code {code})")
+
+
+def _check(code: int, where: str):
+    if code != GEMM_OK:
+        raise GemmError(code, where)
+
+
+def gemm_strerror(code: int) -> str:
+    return _fn("gemm_strerror")(code).decode()
+
+
+def gemm_tile_count() -> int:
+    return _fn("gemm_tile_count")()
+
+
+def gemm_runtime_version() -> int:
+    return _fn("gemm_runtime_version")()
+
+
+def gemm_device_caps_query(device: int = 0) -> gemm_device_caps:
+    caps = gemm_device_caps()
+    _check(_fn("gemm_device_caps_query")(device, ctypes.byref(caps)), "gemm_device_caps_query")
+    return caps
+
+
+def make_caps(num_cus=256, lds_bytes=163840, async_copy=1, wave_size=64, clock_khz=2400000,
+              num_xcds=8, arch=b"gfx950:sramecc+:xnack-") -> gemm_device_caps:
+    """A capability record for host-only planning (no device needed)."""
+    return gemm_device_caps(num_cus, lds_bytes, async_copy, wave_size, clock_khz, num_xcds, arch)
+
+
+def gemm_stage_depth(caps: gemm_device_caps, used: int, tile_bytes, stage_enabled: bool = True) -> int:
+    arr = (ctypes.c_int64 * max(len(tile_bytes), 1))(*tile_bytes)
+    return _fn("gemm_stage_depth")(ctypes.byref(caps), used, arr, len(tile_bytes),
+                                   1 if stage_enabled else 0)
+
+
+def make_desc(M, N, K, in_dtype=F16, out_dtype=F32, epilogue=EPI_NONE, flags=0, batch=1,
+              stride_a=0, stride_b=0, stride_c=0, tile=0) -> gemm_desc:
+    return gemm_desc(M, N, K, in_dtype, out_dtype, epilogue, flags, batch, stride_a, stride_b,
+                     stride_c, tile, 0)
+
+
+class Plan:
+    """Owns a gemm_plan_t; destroyed with the object."""
+
+    def __init__(self, handle: int, desc: gemm_desc):
+        self._h = _vp(handle)
+        self.desc = desc
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> gemm_plan_info:
+        return gemm_plan_get_info(self)
+
+    def describe(self) -> str:
+        return gemm_plan_describe(self)
+
+    def close(self):
+        if self._h and self._h.value:
+            _fn("gemm_plan_destroy")(self._h)
+            self._h = _vp(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gemm_plan(desc: gemm_desc) -> Plan:
+    h = _vp()
+    _check(_fn("gemm_plan")(ctypes.byref(desc), ctypes.byref(h)), "gemm_plan")
+    return Plan(h.value, desc)
+
+
+def gemm_plan_for_caps(desc: gemm_desc, caps: gemm_device_caps) -> Plan:
+    h = _vp()
+    _check(_fn("gemm_plan_for_caps")(ctypes.byref(desc), ctypes.byref(caps), ctypes.byref(h)),
+           "gemm_plan_for_caps")
+    return Plan(h.value, desc)
+
+
+def gemm_plan_get_info(plan: Plan) -> gemm_plan_info:
+    info = gemm_plan_info()
+    _check(_fn("gemm_plan_get_info")(plan.handle, ctypes.byref(info)), "gemm_plan_get_info")
+    return info
+
+
+def gemm_plan_describe(plan: Plan) -> str:
+    return _fn("gemm_plan_describe")(plan.handle).decode()
+
+
+def gemm_plan_destroy(plan: Plan) -> None:
+    plan.close()
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def gemm_run(plan: Plan, A, B, C, stream=None) -> None:
+    """Launch on `stream` (a torch.cuda.Stream, a raw hipStream_t int, or
+    None for torch's current stream).  A, B, C are device tensors or raw
+    device pointers; nothing is synchronised."""
+    if stream is None:
+        s = torch.cuda.current_stream().cuda_stream
+    elif isinstance(stream, int):
+        s = stream
+    else:
+        s = stream.cuda_stream
+    _check(_fn("gemm_run")(plan.handle, _ptr(A), _ptr(B), _ptr(C), s), "gemm_run")
+
+
+def check_runtime() -> None:
+    """The library must run on the HIP runtime torch loaded (one per process)."""
+    v = gemm_runtime_version()
+    hip = torch.version.hip
+    if hip:
+        m = re.match(r"(\d+)\.(\d+)\.(\d+)", hip)
+        if m:
+            want = int(m.group(1)) * 10_000_000 + int(m.group(2)) * 100_000 + int(m.group(3))
+            if v != want:
+                raise RuntimeError(f"libtcgemm.so runs on HIP runtime {v}, torch on {want}: "
+                                   "two HIP runtimes are loaded")

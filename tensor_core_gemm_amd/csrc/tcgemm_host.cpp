@@ -1,0 +1,373 @@
+// Host side of libtcgemm.so: device capabilities, the planner (tile and
+// stage choice) and the C ABI declared in tcgemm.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "tcgemm.h"
+#include "tcgemm_launch.h"
+#include "tcgemm_tiles.h"
+
+namespace {
+
+constexpr uint32_t kPlanMagic = 0x7C6E3A11u;
+
+struct Plan {
+  uint32_t magic;
+  gemm_desc d;
+  gemm_plan_info info;
+  int32_t group_m;
+  int32_t xcd_remap;
+  char text[320];
+};
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("TCGEMM_LOG");
+    return e && *e && *e != '0';
+  }();
+  return on;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int out_size(int dtype) { return dtype == GEMM_F32 ? 4 : 2; }
+
+const tcg::TileDesc& tile_desc(int id) { return tcg::kTiles[id - 1]; }
+
+// Per-device capability cache.
+constexpr int kMaxDevices = 64;
+std::mutex g_caps_mu;
+bool g_caps_valid[kMaxDevices];
+gemm_device_caps g_caps[kMaxDevices];
+int g_caps_rc[kMaxDevices];
+
+int cached_caps(int device, gemm_device_caps* out) {
+  if (device < 0 || device >= kMaxDevices) return GEMM_E_DEVICE;
+  std::lock_guard<std::mutex> lk(g_caps_mu);
+  if (!g_caps_valid[device]) {
+    g_caps_rc[device] = gemm_device_caps_query(device, &g_caps[device]);
+    g_caps_valid[device] = true;
+  }
+  *out = g_caps[device];
+  return g_caps_rc[device];
+}
+
+bool is_gfx950(const gemm_device_caps& c) { return std::strncmp(c.arch, "gfx950", 6) == 0; }
+
+int validate_desc(const gemm_desc* d) {
+  if (!d) return GEMM_E_ARG;
+  if (d->M < 0 || d->N < 0 || d->K < 0 || d->batch < 1) return GEMM_E_ARG;
+  if (d->in_dtype != GEMM_F16 && d->in_dtype != GEMM_BF16) return GEMM_E_DTYPE;
+  if (d->out_dtype != GEMM_F32 && d->out_dtype != GEMM_F16 && d->out_dtype != GEMM_BF16)
+    return GEMM_E_DTYPE;
+  if (d->epilogue != GEMM_EPI_NONE && d->epilogue != GEMM_EPI_RELU) return GEMM_E_ARG;
+  if (d->flags & ~(GEMM_FLAG_FORCE_STAGES_1 | GEMM_FLAG_UNSTAGED)) return GEMM_E_ARG;
+  if (d->tile < 0 || d->tile > tcg::kNumTiles) return GEMM_E_ARG;
+  if (d->reserved != 0) return GEMM_E_ARG;
+  if (d->batch > 1) {
+    if (d->stride_a < d->M * d->K || d->stride_b < d->K * d->N || d->stride_c < d->M * d->N)
+      return GEMM_E_ARG;
+  }
+  return GEMM_OK;
+}
+
+// Relative MFMA throughput of each tile shape on one CU (first estimate,
+// refined by measurement), and how many of its workgroups share a CU.
+double tile_efficiency(int id) {
+  switch (id) {
+    case 1: return 1.00;
+    case 2: return 0.80;
+    case 3: return 0.45;
+    default: return 0.60;
+  }
+}
+int tile_occupancy(int id) {
+  switch (id) {
+    case 1: return 1;
+    case 2: return 2;
+    case 3: return 4;
+    default: return 2;
+  }
+}
+
+// Choose a tile for the problem: short-K products whose N is a multiple of
+// 288 or 96 take the wide-N tiles (one read of A, few trips); the rest take
+// the general tile with the lowest estimated time (whole rounds of
+// workgroups over the CUs times the per-tile MFMA work).
+int choose_tile(const gemm_desc& d, const gemm_device_caps& caps) {
+  if (d.K <= 128 && d.N > 0) {
+    if (d.N % 288 == 0) return 5;
+    if (d.N % 96 == 0) return 4;
+  }
+  int best = 1;
+  double best_t = 1e300;
+  for (int id = 1; id <= 3; ++id) {
+    const auto& t = tile_desc(id);
+    const int64_t tiles = cdiv(d.M, t.bm) * cdiv(d.N, t.bn) * d.batch;
+    const int64_t slots = (int64_t)std::max(caps.num_cus, 1) * tile_occupancy(id);
+    const int64_t rounds = cdiv(std::max<int64_t>(tiles, 1), slots);
+    const double work = (double)t.bm * t.bn * (double)(cdiv(std::max<int64_t>(d.K, 1), t.bk) * t.bk);
+    const double est = (double)rounds * tile_occupancy(id) * work / tile_efficiency(id);
+    if (est < best_t * 0.999) {
+      best_t = est;
+      best = id;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+extern "C" const char* gemm_strerror(int code) {
+  switch (code) {
+    case GEMM_OK: return "success";
+    case GEMM_E_ARG: return "invalid argument (size, stride, flag, tile id or null pointer)";
+    case GEMM_E_DTYPE: return "unsupported storage type (inputs: F16 or BF16; output: F32, F16 or BF16)";
+    case GEMM_E_ALIGN: return "pointer not aligned to its element size";
+    case GEMM_E_ALIAS: return "C overlaps A or B (written parameters may not overlap others)";
+    case GEMM_E_DEVICE: return "no usable gfx950 device, or the plan needs more LDS than it has";
+    case GEMM_E_LAUNCH: return "kernel launch failed";
+    case GEMM_E_NOMEM: return "host allocation failed";
+    case GEMM_E_PLAN: return "null or destroyed plan";
+    case GEMM_E_SIZE: return "problem too large: a tile's byte offsets exceed 31 bits";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int gemm_runtime_version(void) {
+  int v = 0;
+  if (hipRuntimeGetVersion(&v) != hipSuccess) return -1;
+  return v;
+}
+
+extern "C" int gemm_tile_count(void) { return tcg::kNumTiles; }
+
+extern "C" int gemm_device_caps_query(int device, gemm_device_caps* out) {
+  if (!out) return GEMM_E_ARG;
+  std::memset(out, 0, sizeof(*out));
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) {
+    (void)hipGetLastError();
+    return GEMM_E_DEVICE;
+  }
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, device) != hipSuccess) return GEMM_E_DEVICE;
+  out->num_cus = p.multiProcessorCount;
+  out->wave_size = p.warpSize;
+  out->clock_khz = p.clockRate;
+  std::snprintf(out->arch, sizeof(out->arch), "%s", p.gcnArchName);
+  int lds_block = 0, lds_optin = 0;
+  (void)hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
+  (void)hipDeviceGetAttribute(&lds_optin, hipDeviceAttributeSharedMemPerBlockOptin, device);
+  (void)hipGetLastError();
+  out->lds_bytes = std::max<int>({lds_block, lds_optin, (int)p.sharedMemPerBlock});
+  const bool gfx950 = std::strncmp(out->arch, "gfx950", 6) == 0;
+  // gfx950 loads global memory straight into LDS without passing through
+  // registers, so a copy overlaps the MFMAs that read the other slot.
+  out->async_copy = gfx950 ? 1 : 0;
+  out->num_xcds = gfx950 ? 8 : 1;
+  if (log_enabled())
+    std::fprintf(stderr, "[tcgemm] device %d: %s, %d CUs, LDS/workgroup %d (block %d, optin %d), clock %d kHz\n",
+                 device, out->arch, out->num_cus, out->lds_bytes, lds_block, lds_optin, out->clock_khz);
+  return gfx950 ? GEMM_OK : GEMM_E_DEVICE;
+}
+
+extern "C" int gemm_stage_depth(const gemm_device_caps* caps, int64_t used, const int64_t* tile_bytes,
+                                int n_tiles, int stage_enabled) {
+  if (!caps || !stage_enabled || n_tiles <= 0 || !tile_bytes) return 0;
+  if (caps->lds_bytes <= 0 || caps->wave_size <= 0) return 0;
+  int64_t sum = 0;
+  for (int i = 0; i < n_tiles; ++i) {
+    if (tile_bytes[i] < 16) return 0;  // less than one 16-byte copy
+    sum += tile_bytes[i];
+  }
+  const int64_t avail = (int64_t)caps->lds_bytes - std::max<int64_t>(used, 0);
+  if (caps->async_copy && 2 * sum <= avail) return 2;
+  if (sum <= avail) return 1;
+  return 0;
+}
+
+extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps* caps, gemm_plan_t* out) {
+  if (!out) return GEMM_E_ARG;
+  *out = nullptr;
+  int rc = validate_desc(desc);
+  if (rc) return rc;
+  if (!caps || caps->num_cus <= 0 || caps->wave_size != 64) return GEMM_E_DEVICE;
+  gemm_desc d = *desc;
+  if (d.batch == 1) {
+    d.stride_a = d.M * d.K;
+    d.stride_b = d.K * d.N;
+    d.stride_c = d.M * d.N;
+  }
+  const int id = d.tile ? d.tile : choose_tile(d, *caps);
+  const auto& t = tile_desc(id);
+
+  const int64_t tiles[2] = {(int64_t)t.bm * t.bk * 2, (int64_t)t.bk * t.bn * 2};
+  int stages = gemm_stage_depth(caps, 0, tiles, 2, (d.flags & GEMM_FLAG_UNSTAGED) ? 0 : 1);
+  if ((d.flags & GEMM_FLAG_FORCE_STAGES_1) && stages > 1) stages = 1;
+
+  // Byte offsets inside one trip's tiles are 32-bit buffer offsets.
+  if ((int64_t)t.bm * std::max<int64_t>(d.K, 1) * 2 >= (int64_t)0x7fffffff ||
+      (int64_t)t.bk * std::max<int64_t>(d.N, 1) * 2 >= (int64_t)0x7fffffff)
+    return GEMM_E_SIZE;
+  const int64_t tiles_m = cdiv(d.M, t.bm), tiles_n = cdiv(d.N, t.bn);
+  const int64_t wgs = tiles_m * tiles_n * d.batch;
+  const int nt = t.wm * t.wn * 64;
+  if (wgs * nt >= ((int64_t)1 << 32) || cdiv(d.K, t.bk) > 0x7fffffff) return GEMM_E_SIZE;
+
+  Plan* p = new (std::nothrow) Plan();
+  if (!p) return GEMM_E_NOMEM;
+  p->magic = kPlanMagic;
+  p->d = d;
+  gemm_plan_info& in = p->info;
+  in.tile_id = id;
+  in.bm = t.bm;
+  in.bn = t.bn;
+  in.bk = t.bk;
+  in.waves = t.wm * t.wn;
+  in.stages = stages;
+  in.lds_bytes = stages == 0 ? 0 : (int32_t)(stages * (tiles[0] + tiles[1]));
+  in.vec16 = (d.K % 8 == 0 && d.N % 8 == 0 && d.stride_a % 8 == 0 && d.stride_b % 8 == 0) ? 1 : 0;
+  in.tiles_m = tiles_m;
+  in.tiles_n = tiles_n;
+  in.workgroups = wgs;
+  in.trips = cdiv(d.K, t.bk);
+  const int fm = t.bm / t.wm / tcg::kMfmaM, fn = t.bn / t.wn / tcg::kMfmaN;
+  in.mfma_per_run = wgs * in.waves * fm * fn * in.trips * (t.bk / tcg::kMfmaK);
+  in.mfma_m = tcg::kMfmaM;
+  in.mfma_n = tcg::kMfmaN;
+  in.mfma_k = tcg::kMfmaK;
+  p->group_m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(4, tiles_m));
+  p->xcd_remap = caps->num_xcds == 8 ? 1 : 0;
+  std::snprintf(p->text, sizeof(p->text),
+                "tile %d (%dx%dx%d, %d waves), stages %d, LDS %d B, %s copies, grid %lld (%lldx%lld x %lld), "
+                "trips %lld, mfma %dx%dx%d %s, %lld MFMAs",
+                id, t.bm, t.bn, t.bk, in.waves, stages, in.lds_bytes, in.vec16 ? "16-byte" : "element",
+                (long long)wgs, (long long)tiles_m, (long long)tiles_n, (long long)d.batch,
+                (long long)in.trips, in.mfma_m, in.mfma_n, in.mfma_k,
+                d.in_dtype == GEMM_BF16 ? "bf16" : "f16", (long long)in.mfma_per_run);
+  if (log_enabled()) std::fprintf(stderr, "[tcgemm] plan %lldx%lldx%lld: %s\n", (long long)d.M,
+                                  (long long)d.N, (long long)d.K, p->text);
+  *out = reinterpret_cast<gemm_plan_t>(p);
+  return GEMM_OK;
+}
+
+extern "C" int gemm_plan(const gemm_desc* desc, gemm_plan_t* out) {
+  if (!out) return GEMM_E_ARG;
+  *out = nullptr;
+  int rc = validate_desc(desc);
+  if (rc) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_E_DEVICE;
+  }
+  gemm_device_caps caps;
+  rc = cached_caps(dev, &caps);
+  if (rc) return rc;
+  return gemm_plan_for_caps(desc, &caps, out);
+}
+
+static Plan* as_plan(gemm_plan_t h) {
+  Plan* p = reinterpret_cast<Plan*>(h);
+  return (p && p->magic == kPlanMagic) ? p : nullptr;
+}
+
+extern "C" int gemm_plan_get_info(gemm_plan_t plan, gemm_plan_info* out) {
+  Plan* p = as_plan(plan);
+  if (!p) return GEMM_E_PLAN;
+  if (!out) return GEMM_E_ARG;
+  *out = p->info;
+  return GEMM_OK;
+}
+
+extern "C" const char* gemm_plan_describe(gemm_plan_t plan) {
+  Plan* p = as_plan(plan);
+  return p ? p->text : "(invalid plan)";
+}
+
+extern "C" void gemm_plan_destroy(gemm_plan_t plan) {
+  Plan* p = as_plan(plan);
+  if (!p) return;
+  p->magic = 0;
+  delete p;
+}
+
+static bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+  return a0 < b1 && b0 < a1;
+}
+
+extern "C" int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream) {
+  Plan* p = as_plan(plan);
+  if (!p) return GEMM_E_PLAN;
+  const gemm_desc& d = p->d;
+  const gemm_plan_info& in = p->info;
+  if (d.M == 0 || d.N == 0) return GEMM_OK;
+  if (!C || (d.K > 0 && (!A || !B))) return GEMM_E_ARG;
+  const int osz = out_size(d.out_dtype);
+  if (((uintptr_t)A & 1u) || ((uintptr_t)B & 1u) || ((uintptr_t)C & (uintptr_t)(osz - 1)))
+    return GEMM_E_ALIGN;
+  // Written parameters may not overlap the others (page "Module Tolk.Uniform", precondition).
+  const uintptr_t c0 = (uintptr_t)C;
+  const uintptr_t c1 = c0 + (uintptr_t)(((d.batch - 1) * d.stride_c + d.M * d.N) * osz);
+  if (d.K > 0) {
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((d.batch - 1) * d.stride_a + d.M * d.K) * 2);
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((d.batch - 1) * d.stride_b + d.K * d.N) * 2);
+    if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return GEMM_E_ALIAS;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_E_DEVICE;
+  }
+  gemm_device_caps caps;
+  if (cached_caps(dev, &caps) != GEMM_OK || !is_gfx950(caps) || caps.lds_bytes < in.lds_bytes)
+    return GEMM_E_DEVICE;
+
+  tcg::KArgs a;
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.C = C;
+  a.M = d.M;
+  a.N = d.N;
+  a.K = d.K;
+  a.stride_a = d.stride_a;
+  a.stride_b = d.stride_b;
+  a.stride_c = d.stride_c;
+  a.tiles_m = in.tiles_m;
+  a.tiles_n = in.tiles_n;
+  a.workgroups = in.workgroups;
+  a.trips = (int32_t)in.trips;
+  a.out_dtype = d.out_dtype;
+  a.relu = d.epilogue == GEMM_EPI_RELU ? 1 : 0;
+  a.group_m = p->group_m;
+  a.xcd_remap = p->xcd_remap;
+  a.vec_store4 = (d.N % 4 == 0 && (c0 % (uintptr_t)(4 * osz)) == 0 && (d.batch == 1 || d.stride_c % 4 == 0)) ? 1 : 0;
+  const int64_t per16 = 16 / osz;
+  a.vec_store16 = (d.N % per16 == 0 && (c0 % 16u) == 0 && (d.batch == 1 || d.stride_c % per16 == 0)) ? 1 : 0;
+  const bool vec16 = in.vec16 && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
+  const bool bf16 = d.in_dtype == GEMM_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipErrorInvalidValue;
+  switch (in.tile_id) {
+    case 1: e = tcg::launch_t1(in.stages, vec16, bf16, a, s); break;
+    case 2: e = tcg::launch_t2(in.stages, vec16, bf16, a, s); break;
+    case 3: e = tcg::launch_t3(in.stages, vec16, bf16, a, s); break;
+    case 4: e = tcg::launch_t4(in.stages, vec16, bf16, a, s); break;
+    case 5: e = tcg::launch_t5(in.stages, vec16, bf16, a, s); break;
+    default: break;
+  }
+  if (e != hipSuccess) {
+    if (log_enabled()) std::fprintf(stderr, "[tcgemm] launch failed: %s\n", hipGetErrorString(e));
+    return GEMM_E_LAUNCH;
+  }
+  return GEMM_OK;
+}

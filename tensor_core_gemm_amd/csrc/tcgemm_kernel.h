@@ -1,0 +1,567 @@
+// Device code of the GEMM: C = epilogue(A . B) on gfx950 MFMA units.
+//
+// One kernel template serves three paths that issue the same MFMA sequence
+// on the same values, so their results are bit-identical (page "Module
+// Tolk.Stage": staging moves values and never rounds them):
+//
+//   STAGES = 2  two LDS slots: chunk t+1 is copied into slot (t+1) mod 2
+//               while slot t mod 2 feeds the MFMAs; one barrier per trip
+//               (page "Module Tolk.Stage", "Two stages");
+//   STAGES = 1  one slot: copy at the start of the trip, barrier, compute,
+//               barrier (the single-stage case of the same page);
+//   STAGES = 0  unstaged: every wave loads its fragments straight from
+//               global memory, a few bytes at a time (the "Setting.stage
+//               off" case).
+//
+// Copies move 16 bytes per lane (VEC16: a buffer load that writes LDS
+// directly, gfx950's asynchronous global->LDS copy) or, for operands whose
+// rows are not 16-byte aligned, 8 element loads per lane followed by one
+// 16-byte LDS write.  Either way a lane owns the same LDS chunk positions,
+// so the LDS image is the same.
+//
+// Out-of-range elements read 0 (page "gizml:tile", In.at): masked lanes use
+// a buffer offset past the resource's size, which the buffer unit turns into
+// a zero read.  Out-of-range outputs are not written (Out.put).
+//
+// Trip counts are the same for every lane of a workgroup, so every barrier
+// and MFMA runs in uniform control flow (page "Module Tolk.Uniform").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tcgemm_kernel_args.h"
+#include "tcgemm_tiles.h"
+
+namespace tcg {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr uint32_t kOOB = 0x80000000u;  // a byte offset no resource here reaches
+constexpr int kOutF32 = 0, kOutF16 = 4, kOutBF16 = 5;
+
+// ---------------------------------------------------------------------------
+// LDS layout: row-major slot, 16-byte chunks, chunk index XOR-swizzled by a
+// function of the row.  The XOR value stays below the row's power-of-two
+// chunk group, so the map is a bijection inside every row.
+template <int CPR>
+__device__ __forceinline__ int swz_a(int r) {
+  return r & swizzle_mask(CPR);
+}
+template <int CPR>
+__device__ __forceinline__ int swz_b(int r) {
+  // rows 4q .. 4q+3 are XORed with 0, 6, 10, 12 (reduced to the row's mask)
+  const int t = (0xCA60 >> (4 * (r & 3))) & 15;
+  return t & swizzle_mask(CPR);
+}
+
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+template <bool BF16IN>
+__device__ __forceinline__ f32x16 mfma(const u32x4& src0, const u32x4& src1, const f32x16& acc) {
+  if constexpr (BF16IN)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, src0),
+                                                   __builtin_bit_cast(bf16x8, src1), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, src0),
+                                                  __builtin_bit_cast(f16x8, src1), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
+
+// ---------------------------------------------------------------------------
+// Where a workgroup works: (batch item, tile row, tile column).
+struct TilePos {
+  int64_t b, tm, tn;
+};
+
+__device__ __forceinline__ TilePos tile_of(const KArgs& a) {
+  int64_t wg = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin; renumber so that the
+  // workgroups on one XCD take consecutive tiles (which share A rows and B
+  // columns in that XCD's L2).
+  if (a.xcd_remap) {
+    const int64_t q = a.workgroups / 8;
+    if (wg < 8 * q) wg = (wg % 8) * q + wg / 8;
+  }
+  const int64_t per_batch = a.tiles_m * a.tiles_n;
+  TilePos p;
+  p.b = wg / per_batch;
+  const int64_t t = wg - p.b * per_batch;
+  // grouped order: group_m tile rows at a time, column-major inside a group
+  const int64_t in_group = (int64_t)a.group_m * a.tiles_n;
+  const int64_t g = t / in_group;
+  const int64_t first = g * a.group_m;
+  const int64_t gsize = (a.tiles_m - first) < a.group_m ? (a.tiles_m - first) : a.group_m;
+  const int64_t r = t - g * in_group;
+  p.tm = first + r % gsize;
+  p.tn = r / gsize;
+  return p;
+}
+
+
+// ---------------------------------------------------------------------------
+// Epilogue helpers.
+__device__ __forceinline__ float relu_if(float v, int relu) {
+  return relu ? (v > 0.0f ? v : 0.0f) : v;  // Tile.relu: NaN and -0 give +0
+}
+
+__device__ __forceinline__ uint16_t to_out16(float v, int out_dtype) {
+  return out_dtype == kOutBF16 ? __builtin_bit_cast(uint16_t, (__bf16)v)
+                               : __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Unstaged kernel: each lane stores its four consecutive columns directly.
+template <class T>
+__device__ __forceinline__ void store_direct(const KArgs& a, const f32x16 (&acc)[T::FM][T::FN], int64_t b,
+                                             int64_t m0, int64_t n0, int lane) {
+  const int64_t M = a.M, N = a.N;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const int64_t m = m0 + 32 * i + (lane & 31);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + 32 * j + 8 * g + 4 * (lane >> 5);
+        if (n >= N) continue;
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[q] = relu_if(acc[i][j][4 * g + q], a.relu);
+        const int64_t idx = b * a.stride_c + m * N + n;
+        const bool full = a.vec_store4 && (n + 4 <= N);
+        if (a.out_dtype == kOutF32) {
+          float* Cp = (float*)a.C + idx;
+          if (full) {
+            *(f32x4*)Cp = f32x4{y[0], y[1], y[2], y[3]};
+          } else {
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) Cp[q] = y[q];
+          }
+        } else {
+          uint16_t h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h[q] = to_out16(y[q], a.out_dtype);
+          uint16_t* Cp = (uint16_t*)a.C + idx;
+          if (full) {
+            *(u32x2*)Cp = u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+          } else {
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) Cp[q] = h[q];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Staged kernels: each wave writes a 32-row band of its outputs (EPW
+// columns, already rounded) into its own LDS region, then reads the band
+// back row by row and stores 16 bytes per lane, so each store instruction
+// writes whole row segments.
+template <class T>
+__device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (&acc)[T::FM][T::FN], int64_t b,
+                                                  int64_t m0, int64_t n0, int lane, int w, char* smem) {
+  constexpr int EPW = T::EPW, EPJ = EPW / 32;
+  const int64_t M = a.M, N = a.N;
+  const int osz = a.out_dtype == kOutF32 ? 4 : 2;
+  const int pitch = EPW * osz + 16;  // bytes per band row (padded against bank conflicts)
+  lds_char* band = (lds_char*)smem + w * T::EPI_WAVE_BYTES;
+  const int cpr = EPW * osz / 16;  // 16-byte chunks per band row
+  const int per_elem = 16 / osz;   // elements per chunk
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+#pragma unroll
+    for (int jb = 0; jb < T::FN / EPJ; ++jb) {
+      const int row = lane & 31;
+#pragma unroll
+      for (int jj = 0; jj < EPJ; ++jj) {
+        const int j = jb * EPJ + jj;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * jj + 8 * g + 4 * (lane >> 5);
+          float y[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] = relu_if(acc[i][j][4 * g + q], a.relu);
+          if (osz == 4) {
+            *(__attribute__((address_space(3))) f32x4*)(band + row * pitch + col * 4) = f32x4{y[0], y[1], y[2], y[3]};
+          } else {
+            const uint32_t lo = pack2(to_out16(y[0], a.out_dtype), to_out16(y[1], a.out_dtype));
+            const uint32_t hi = pack2(to_out16(y[2], a.out_dtype), to_out16(y[3], a.out_dtype));
+            *(__attribute__((address_space(3))) u32x2*)(band + row * pitch + col * 2) = u32x2{lo, hi};
+          }
+        }
+      }
+      // Same-wave LDS accesses complete in order: the band is readable now.
+      const int64_t mb = m0 + 32 * i;
+      const int64_t nb = n0 + EPW * jb;
+      const int chunks = 32 * cpr;
+      for (int idx = lane; idx < chunks; idx += 64) {
+        const int r = idx / cpr;
+        const int ch = idx - r * cpr;
+        const u32x4 v = *(const lds_u32x4*)(band + r * pitch + ch * 16);
+        const int64_t m = mb + r;
+        const int64_t n = nb + (int64_t)ch * per_elem;
+        if (m >= M || n >= N) continue;
+        char* dst = (char*)a.C + (b * a.stride_c + m * N + n) * osz;
+        if (a.vec_store16 && n + per_elem <= N) {
+          *(u32x4*)dst = v;
+        } else {
+          const int cnt = (int)((N - n) < per_elem ? (N - n) : per_elem);
+          if (osz == 4) {
+            for (int q = 0; q < cnt; ++q) ((uint32_t*)dst)[q] = v[q];
+          } else {
+            for (int q = 0; q < cnt; ++q) ((uint16_t*)dst)[q] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+template <int TID, int STAGES, bool VEC16, bool BF16IN>
+__global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
+  using T = Tile<TID>;
+  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, NW = T::NW, NT = T::NT;
+  constexpr int FM = T::FM, FN = T::FN, KS = T::KS, WN = T::WN;
+  constexpr int CPR_A = T::CPR_A, CPR_B = T::CPR_B;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (w / WN) * T::WTM;  // wave tile origin inside the workgroup tile
+  const int wn0 = (w % WN) * T::WTN;
+
+  const TilePos tp = tile_of(a);
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const int64_t row0 = tp.tm * BM;
+  const int64_t col0 = tp.tn * BN;
+  const uint16_t* __restrict__ Ab = a.A + tp.b * a.stride_a;
+  const uint16_t* __restrict__ Bb = a.B + tp.b * a.stride_b;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;  // Program.zeros
+
+  const int trips = a.trips;
+  char* smem_epi = nullptr;
+  (void)smem_epi;
+
+  if constexpr (STAGES == 0) {
+    // ---------------- unstaged: fragments straight from global memory -----
+    for (int t = 0; t < trips; ++t) {
+      const int64_t k0 = (int64_t)t * BK;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + row0 * K + k0, ((M - row0) * K - k0) * 2);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + k0 * N + col0, ((K - k0) * N - col0) * 2);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int kk = s * 16 + 8 * (lane >> 5);  // this lane's first k inside the trip
+        u32x4 af[FM], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm0 + 32 * i + (lane & 31);
+          const bool rok = row0 + r < M;
+          const uint32_t off = (uint32_t)(r * K + kk) * 2u;
+          if constexpr (VEC16) {
+            const bool ok = rok && (k0 + kk < K);
+            af[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? off : kOOB, 0, 0);
+          } else {
+            uint32_t e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const bool ok = rok && (k0 + kk + q < K);
+              e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, ok ? off + 2u * q : kOOB, 0, 0);
+            }
+            af[i] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int c = wn0 + 32 * j + (lane & 31);
+          const bool cok = col0 + c < N;
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const bool ok = cok && (k0 + kk + q < K);
+            const uint32_t off = (uint32_t)((kk + q) * N + c) * 2u;
+            e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, ok ? off : kOOB, 0, 0);
+          }
+          bfr[j] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma<BF16IN>(bfr[j], af[i], acc[i][j]);
+      }
+    }
+  } else {
+    // ---------------- staged through LDS ----------------------------------
+    // slot0 also holds the epilogue's output bands after the last trip.
+    __shared__ __attribute__((aligned(1024))) char slot0[T::SLOT > T::EPI_BYTES ? T::SLOT : T::EPI_BYTES];
+    __shared__ __attribute__((aligned(1024))) char slot1[STAGES == 2 ? T::SLOT : 16];
+    smem_epi = slot0;
+
+    // Copy plan.  Lane position P = i*NT + tid of a slot's chunk array holds
+    // the logical chunk (r, c) of the tile with c = (P mod CPR) ^ swz(r): the
+    // swizzle is applied on the global side, so each wave writes 1 KiB of LDS
+    // contiguously.  Where NT is a multiple of CPR and of the swizzle period,
+    // c does not depend on the round i and the byte offset is a per-lane base
+    // plus a uniform step per round.
+    //
+    // Zero-fill: each trip's buffer resource ends exactly at the operand's
+    // last element, so A rows past M and B rows past K are out of range and
+    // read 0 by themselves; the K tail of A (last trip) and the N tail of B
+    // (last tile column) are masked with an out-of-range offset.
+    const bool b_ntail = col0 + BN > N;
+    constexpr bool SIMPLE_A = (NT % CPR_A == 0) && ((NT / CPR_A) % (swizzle_mask(CPR_A) + 1) == 0) &&
+                              (T::CH_A % NT == 0);
+    constexpr bool SIMPLE_B = (NT % CPR_B == 0) && ((NT / CPR_B) % 4 == 0) && (T::CH_B % NT == 0);
+    // Per-lane chunk of round 0 (rounds add NT / CPR rows).
+    const int a_r0 = tid / CPR_A;
+    const int a_c80 = 8 * ((tid % CPR_A) ^ swz_a<CPR_A>(a_r0));
+    const uint32_t a_off0 = (uint32_t)(a_r0 * K + a_c80) * 2u;
+    const int b_r0 = tid / CPR_B;
+    const int b_c80 = 8 * ((tid % CPR_B) ^ swz_b<CPR_B>(b_r0));
+    const uint32_t b_off0 = (uint32_t)(b_r0 * N + b_c80) * 2u;
+    auto copy = [&](int t, char* slot) __attribute__((always_inline)) {
+      const int64_t k0 = (int64_t)t * BK;
+      const bool ktail = k0 + BK > K;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + row0 * K + k0, ((M - row0) * K - k0) * 2);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + k0 * N + col0, ((K - k0) * N - col0) * 2);
+#pragma unroll
+      for (int i = 0; i < T::IA; ++i) {
+        if (T::CH_A % NT == 0 || (i * NW + w) * 64 < T::CH_A) {  // whole waves only
+          int c8;
+          uint32_t off;
+          if constexpr (SIMPLE_A) {
+            c8 = a_c80;
+            off = a_off0 + (uint32_t)(i * (NT / CPR_A) * K * 2);
+          } else {
+            const int P = i * NT + tid;
+            const int r = P / CPR_A;
+            c8 = 8 * ((P % CPR_A) ^ swz_a<CPR_A>(r));
+            off = (uint32_t)(r * K + c8) * 2u;
+          }
+          char* dst = slot + (i * NW + w) * 1024;
+          if constexpr (VEC16) {
+            const uint32_t o = (ktail && k0 + c8 >= K) ? kOOB : off;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)dst, 16, o, 0, 0, 0);
+          } else {
+            uint32_t e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const bool ok = k0 + c8 + q < K;
+              e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, ok ? off + 2u * q : kOOB, 0, 0);
+            }
+            *(lds_u32x4*)((lds_char*)dst + lane * 16) =
+                u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+          }
+        }
+      }
+      char* slotb = slot + T::A_BYTES;
+#pragma unroll
+      for (int i = 0; i < T::IB; ++i) {
+        if (T::CH_B % NT == 0 || (i * NW + w) * 64 < T::CH_B) {
+          int c8;
+          uint32_t off;
+          if constexpr (SIMPLE_B) {
+            c8 = b_c80;
+            off = b_off0 + (uint32_t)(i * (NT / CPR_B) * N * 2);
+          } else {
+            const int P = i * NT + tid;
+            const int r = P / CPR_B;
+            c8 = 8 * ((P % CPR_B) ^ swz_b<CPR_B>(r));
+            off = (uint32_t)(r * N + c8) * 2u;
+          }
+          char* dst = slotb + (i * NW + w) * 1024;
+          if constexpr (VEC16) {
+            const uint32_t o = (b_ntail && col0 + c8 >= N) ? kOOB : off;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)dst, 16, o, 0, 0, 0);
+          } else {
+            uint32_t e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const bool ok = col0 + c8 + q < N;
+              e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, ok ? off + 2u * q : kOOB, 0, 0);
+            }
+            *(lds_u32x4*)((lds_char*)dst + lane * 16) =
+                u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+          }
+        }
+      }
+    };
+
+    // Fragments of one k-step (s) from a slot.
+    //
+    // A fragment (block i, k-step s): lane l reads row wm0 + 32i + (l mod 32)
+    // at logical chunk 2s + l/32, i.e. 8 k-contiguous values.  The row's
+    // swizzle depends only on l (wm0 and 32i are multiples of the swizzle
+    // period), so the lane's byte offset is a_base[s] + i * 32 * BK * 2.
+    //
+    // B fragment (block j, k-step s): column (l mod 32) and 8 k-values
+    // 16s + 8(l/32) + e, read as two transposing 4-value reads (h = 0, 1).
+    // ds_read_b64_tr_b16 works on groups of 16 lanes: lane x of a group
+    // receives element x mod 4 of the reads of lanes 4e + x/4, e = 0..3.  So
+    // lane 4e + q reads row e of the group's 4 x 16 block at columns
+    // 4q .. 4q+3, and lane x receives column x.  The row is
+    // 16s + 8(l/32) + 4h + ((l mod 16) / 4), whose swizzle depends only on
+    // l, so the lane's byte offset is b_base[j] + (16s + 4h) * BN * 2.
+    int a_base[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int r = wm0 + (lane & 31);
+      const int c = 2 * s + (lane >> 5);
+      a_base[s] = r * (BK * 2) + ((c ^ swz_a<CPR_A>(r)) * 16);
+    }
+    int b_base[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
+      const int colq = wn0 + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      b_base[j] = r * (BN * 2) + (((colq >> 3) ^ swz_b<CPR_B>(r)) * 16) + ((colq >> 2) & 1) * 8;
+    }
+    struct Frags {
+      u32x4 a[FM], b[FN];
+    };
+    auto load = [&](const char* slot, int s, Frags& f) __attribute__((always_inline)) {
+      const lds_char* sa = (const lds_char*)slot;
+      const lds_char* sb = (const lds_char*)slot + T::A_BYTES;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        f.a[i] = *(const lds_u32x4*)(sa + a_base[s] + i * (32 * BK * 2));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        uint32_t v[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const lds_char* p = sb + b_base[j] + (16 * s + 4 * h) * (BN * 2);
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          v[2 * h] = pack2((uint16_t)x[0], (uint16_t)x[1]);
+          v[2 * h + 1] = pack2((uint16_t)x[2], (uint16_t)x[3]);
+        }
+        f.b[j] = u32x4{v[0], v[1], v[2], v[3]};
+      }
+    };
+    auto mma = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma<BF16IN>(f.b[j], f.a[i], acc[i][j]);
+    };
+    auto wait_all_and_barrier = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+
+    Frags f0, f1;
+    if constexpr (STAGES == 2) {
+      // Trip t reads slot t mod 2 while chunk t+1 lands in the other slot.
+      // The one barrier of a trip comes after the last k-step's fragments
+      // are in registers and this wave's copy has landed: it retires every
+      // read of slot t mod 2 before trip t+1 overwrites it, and publishes
+      // chunk t+1 before it is read.  The last k-step's MFMAs then run while
+      // the first fragments of chunk t+1 load.
+      auto trip = [&](int t, char* cur, char* nxt) __attribute__((always_inline)) {
+        // The copy is issued first and kept there: the scheduler may not
+        // sink it towards the barrier, where it would no longer overlap.
+        if (t + 1 < trips) copy(t + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          Frags& now = (s & 1) ? f1 : f0;
+          Frags& next = (s & 1) ? f0 : f1;
+          if (s + 1 < KS) {
+            load(cur, s + 1, next);
+            mma(now);
+          } else {
+            wait_all_and_barrier();
+            if (t + 1 < trips) load(nxt, 0, next);
+            mma(now);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (trips > 0) {
+        copy(0, slot0);
+        wait_all_and_barrier();
+        load(slot0, 0, f0);
+      }
+      // Unrolled by two so that each copy and each read names one slot;
+      // an odd last trip is peeled so the loop body has no branch around a
+      // whole trip.  KS is even, so every trip starts with its fragments in f0.
+      static_assert(KS % 2 == 0, "k-steps per trip must be even");
+      int t = 0;
+      for (; t + 1 < trips; t += 2) {
+        trip(t, slot0, slot1);
+        trip(t + 1, slot1, slot0);
+      }
+      if (t < trips) trip(t, slot0, slot1);
+    } else {
+      for (int t = 0; t < trips; ++t) {
+        copy(t, slot0);
+        wait_all_and_barrier();  // publishes the tile
+        load(slot0, 0, f0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          Frags& now = (s & 1) ? f1 : f0;
+          Frags& next = (s & 1) ? f0 : f1;
+          if (s + 1 < KS) load(slot0, s + 1, next);
+          mma(now);
+        }
+        __syncthreads();  // retires the reads before the next copy
+      }
+    }
+  }
+
+  // ---------------- epilogue: relu, rounding, masked store ----------------
+  // Lane l of MFMA block (i, j) holds, in registers 4g .. 4g+3, the four
+  // consecutive columns 8g + 4(l/32) + 0..3 of row (l mod 32).
+  if constexpr (STAGES == 0) {
+    store_direct<T>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane);
+  } else {
+    store_through_lds<T>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane, w, smem_epi);
+  }
+}
+
+// Launch one instantiation: returns hipGetLastError's result.
+template <int TID, int STAGES, bool VEC16, bool BF16IN>
+hipError_t launch_one(const KArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_kernel<TID, STAGES, VEC16, BF16IN>), dim3((uint32_t)a.workgroups),
+                     dim3(Tile<TID>::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int TID>
+hipError_t launch_tile(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s) {
+#define TCG_CASE(ST, V, BF) \
+  if (stages == ST && vec16 == V && bf16 == BF) return launch_one<TID, ST, V, BF>(a, s);
+  TCG_CASE(2, true, true) TCG_CASE(2, true, false) TCG_CASE(2, false, true) TCG_CASE(2, false, false)
+  TCG_CASE(1, true, true) TCG_CASE(1, true, false) TCG_CASE(1, false, true) TCG_CASE(1, false, false)
+  TCG_CASE(0, true, true) TCG_CASE(0, true, false) TCG_CASE(0, false, true) TCG_CASE(0, false, false)
+#undef TCG_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tcg

@@ -1,0 +1,75 @@
+// Tile configurations shared by the planner (host) and the kernels (device).
+//
+// A workgroup computes a BM x BN block of C with WM x WN waves (64 lanes
+// each); each wave owns a (BM/WM) x (BN/WN) sub-block made of 32 x 32 MFMA
+// blocks.  K advances BK per trip (page "gizml:tile": the worked example
+// folds over K in blocks; page "Module Tolk.Stage", tile: a workgroup of
+// 2 x 2 warps, K unrolled per trip).  On gfx950 a compute unit also has four
+// SIMDs, so 2 x 2 waves per workgroup keeps one wave on each.
+#pragma once
+
+#include <stdint.h>
+
+namespace tcg {
+
+struct TileDesc {
+  int id;
+  int bm, bn, bk;
+  int wm, wn;  // wave grid
+};
+
+// id 0 is "planner's choice" in the ABI; real ids start at 1.
+constexpr TileDesc kTiles[] = {
+    {1, 256, 256, 64, 2, 2},  // wave 128 x 128: large MFMA-bound products
+    {2, 128, 128, 64, 2, 2},  // wave 64 x 64: mid sizes / more workgroups
+    {3, 64, 64, 64, 2, 2},    // wave 32 x 32: small and ragged products
+    {4, 256, 96, 32, 4, 1},   // wave 64 x 96: short-K, N a multiple of 96
+    {5, 128, 288, 32, 4, 1},  // wave 32 x 288: short-K, N = 288 in one tile
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+constexpr int kMfmaM = 32, kMfmaN = 32, kMfmaK = 16;  // v_mfma_f32_32x32x16_{bf16,f16}
+
+// Compile-time view of one configuration.
+template <int ID>
+struct Tile {
+  static constexpr TileDesc d = kTiles[ID - 1];
+  static constexpr int BM = d.bm, BN = d.bn, BK = d.bk, WM = d.wm, WN = d.wn;
+  static constexpr int NW = WM * WN;            // waves per workgroup
+  static constexpr int NT = NW * 64;            // lanes per workgroup
+  static constexpr int WTM = BM / WM;           // wave tile rows
+  static constexpr int WTN = BN / WN;           // wave tile columns
+  static constexpr int FM = WTM / kMfmaM;       // MFMA blocks per wave along M
+  static constexpr int FN = WTN / kMfmaN;       // MFMA blocks per wave along N
+  static constexpr int KS = BK / kMfmaK;        // MFMA k-steps per trip
+  static constexpr int CPR_A = BK / 8;          // 16-byte chunks per A row (K-contiguous)
+  static constexpr int CPR_B = BN / 8;          // 16-byte chunks per B row (N-contiguous)
+  static constexpr int CH_A = BM * CPR_A;       // chunks in one A slot
+  static constexpr int CH_B = BK * CPR_B;       // chunks in one B slot
+  static constexpr int IA = (CH_A + NT - 1) / NT;  // copy rounds per lane for A
+  static constexpr int IB = (CH_B + NT - 1) / NT;  // copy rounds per lane for B
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BK * BN * 2;
+  static constexpr int SLOT = A_BYTES + B_BYTES;
+  // Epilogue band: 32 rows x EPW columns per wave (EPW a multiple of 32
+  // dividing WTN), fp32 worst case, rows padded by 16 bytes; the bands of
+  // all waves must fit in the first LDS slot (or a little more).
+  static constexpr int epw_for(int avail) {
+    int best = 32;
+    for (int e = 32; e <= WTN; e += 32)
+      if (WTN % e == 0 && NW * 32 * (e * 4 + 16) <= avail) best = e;
+    return best;
+  }
+  static constexpr int EPW = epw_for(SLOT);
+  static constexpr int EPI_WAVE_BYTES = 32 * (EPW * 4 + 16);
+  static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
+  static_assert(WTM % kMfmaM == 0 && WTN % kMfmaN == 0, "wave tile must be MFMA blocks");
+  static_assert(BK % kMfmaK == 0 && BK % 8 == 0, "BK must be whole k-steps and chunks");
+  static_assert(BN % 8 == 0, "BN must be whole chunks");
+};
+
+// Largest power of two dividing n, minus one: the XOR mask that keeps a
+// swizzled chunk index inside its row when a row has n chunks.
+constexpr int swizzle_mask(int n) { return (n & -n) - 1; }
+
+}  // namespace tcg

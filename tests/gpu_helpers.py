@@ -1,0 +1,106 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C
+ABI and compare with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import gemm_workloads as gw
+import oracle
+
+TOL = 1e-2  # max relative error on non-integer inputs (fp16/bf16 in, fp32 accumulate)
+
+
+def note(msg):
+    """Name the case before a GPU step (so a crash log says what ran)."""
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def out_torch(dtype):
+    return gw.TORCH_DTYPE[dtype]
+
+
+def run(tcg, A, B, w, flags=0, tile=0, guard=0, sentinel=None, plan=None, a_offset=0,
+        b_offset=0):
+    """Run C = epilogue(A.B) on the GPU; A, B are CPU tensors.  With guard > 0
+    the output sits inside a larger buffer filled with `sentinel` bits;
+    returns (C, whole buffer) on the CPU.  a_offset/b_offset shift the
+    operands by that many elements inside their device buffers."""
+    dev = torch.device("cuda")
+    Ad = torch.empty(A.numel() + a_offset, dtype=A.dtype, device=dev)
+    Ad[a_offset:].copy_(A.reshape(-1))
+    Bd = torch.empty(B.numel() + b_offset, dtype=B.dtype, device=dev)
+    Bd[b_offset:].copy_(B.reshape(-1))
+    n_out = w.batch * w.M * w.N
+    odt = out_torch(w.out_dtype)
+    buf = torch.empty(n_out + 2 * guard, dtype=odt, device=dev)
+    if sentinel is not None:
+        buf.view(torch.int32 if odt == torch.float32 else torch.int16).fill_(sentinel)
+    else:
+        buf.zero_()
+    C = buf[guard:guard + n_out]
+    if plan is None:
+        plan = tcg.gemm_plan(tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
+                                           flags, w.batch,
+                                           w.M * w.K if w.batch > 1 else 0,
+                                           w.K * w.N if w.batch > 1 else 0,
+                                           w.M * w.N if w.batch > 1 else 0, tile))
+    note(f"{w.name} M={w.M} N={w.N} K={w.K} batch={w.batch} flags={flags} tile={tile} "
+         f"plan: {plan.describe()}")
+    tcg.gemm_run(plan, Ad[a_offset:] if a_offset else Ad, Bd[b_offset:] if b_offset else Bd, C)
+    torch.cuda.synchronize()
+    shape = (w.batch, w.M, w.N)
+    return C.cpu().reshape(shape), buf.cpu(), plan
+
+
+def as_bits(C):
+    """Output tensor -> numpy array of raw bits (for bitwise comparisons)."""
+    t = C.contiguous()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy()
+    return t.view(torch.int16).numpy()
+
+
+def as_values(C):
+    return C.float().numpy()
+
+
+def rel_errors(c, y, sigma):
+    """|c - y| / max(|y|, 0.01 sigma): relative error with a floor at one
+    hundredth of an output's standard deviation (half of the relu outputs
+    are 0, where a plain relative error is undefined)."""
+    c = np.asarray(c, np.float64)
+    y = np.asarray(y, np.float64)
+    return np.abs(c - y) / np.maximum(np.abs(y), 0.01 * sigma)
+
+
+def check_against_oracle(w, A, B, C):
+    """Full comparison: exact for integer workloads, TOL otherwise."""
+    Cref, Y = oracle.gemm(A, B, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
+                          batch=w.batch, want_y=True)
+    got = as_values(C)
+    if w.exact:
+        want = oracle.to_float(w.out_dtype, Cref)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{w.name}: {len(bad)} mismatches, first at {bad[:5].tolist()}"
+        return 0.0
+    assert np.all(np.isfinite(got)), f"{w.name}: non-finite output"
+    err = rel_errors(got, Y, w.sigma_out())
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= TOL, f"{w.name}: max rel err {worst:.3e} at {np.unravel_index(err.argmax(), err.shape)}"
+    return worst
+
+
+def check_sampled(w, A, B, C, count=4096, seed=123):
+    bi, ii, jj = gw.sample_indices(w.M, w.N, count, seed, w.batch)
+    out, Y = oracle.gemm_sampled(A, B, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, bi, ii,
+                                 jj, batch=w.batch)
+    got = as_values(C)[bi, ii, jj]
+    if w.exact:
+        assert np.array_equal(got, oracle.to_float(w.out_dtype, out))
+        return 0.0
+    err = rel_errors(got, Y, w.sigma_out())
+    worst = float(err.max())
+    assert worst <= TOL, f"{w.name}: sampled max rel err {worst:.3e}"
+    return worst

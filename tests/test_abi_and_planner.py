@@ -1,0 +1,167 @@
+"""Host-only checks of libtcgemm.so: it loads, exports every entry point the
+headers declare, and its planner (tile, stage and grid decisions, argument
+validation) behaves as specified -- no GPU needed (capabilities injected)."""
+import os
+import re
+
+import pytest
+
+import tensor_core_gemm_amd as tcg
+from tensor_core_gemm_amd import BF16, EPI_NONE, EPI_RELU, F16, F32
+
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(INCLUDE)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text,
+                             re.M):
+            names.append(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"gemm_plan", "gemm_run", "gemm_plan_describe", "gemm_plan_destroy",
+            "gemm_strerror", "tcg_probe_mfma", "tcg_probe_ds_read_tr16"} <= set(names)
+    lib = tcg.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_strerror_names_every_code():
+    for code in range(0, -10, -1):
+        assert "unknown" not in tcg.gemm_strerror(code)
+    assert "unknown" in tcg.gemm_strerror(-100)
+
+
+CAPS = tcg.make_caps()
+
+
+def plan(M, N, K, in_dtype=BF16, out_dtype=BF16, epi=EPI_RELU, flags=0, batch=1, tile=0,
+         caps=CAPS, **strides):
+    d = tcg.make_desc(M, N, K, in_dtype, out_dtype, epi, flags, batch,
+                      strides.get("sa", 0), strides.get("sb", 0), strides.get("sc", 0), tile)
+    return tcg.gemm_plan_for_caps(d, caps)
+
+
+def test_stage_depth_rule():
+    """Page "Module Tolk.Stage", depth: 2 with async copies where two stages
+    fit, 1 where one does, 0 where none does, where no tile is given, where
+    a tile is below one 16-byte copy, or where staging is off."""
+    caps = tcg.make_caps(lds_bytes=163840)
+    slot = [32768, 32768]
+    assert tcg.gemm_stage_depth(caps, 0, slot) == 2
+    assert tcg.gemm_stage_depth(caps, 90000, slot) == 1       # 73840 left: one slot of 65536
+    assert tcg.gemm_stage_depth(caps, 100000, slot) == 0      # 63840 left: none
+    assert tcg.gemm_stage_depth(tcg.make_caps(async_copy=0), 0, slot) == 1
+    assert tcg.gemm_stage_depth(caps, 0, []) == 0
+    assert tcg.gemm_stage_depth(caps, 0, [8, 4096]) == 0
+    assert tcg.gemm_stage_depth(caps, 0, slot, stage_enabled=False) == 0
+    assert tcg.gemm_stage_depth(tcg.make_caps(lds_bytes=0), 0, slot) == 0
+    assert tcg.gemm_stage_depth(tcg.make_caps(wave_size=0), 0, slot) == 0
+    # exactly full
+    assert tcg.gemm_stage_depth(tcg.make_caps(lds_bytes=131072), 0, [65536, 65536]) == 1
+    assert tcg.gemm_stage_depth(tcg.make_caps(lds_bytes=262144), 0, [65536, 65536]) == 2
+
+
+def test_headline_plan():
+    p = plan(4096, 4096, 4096)
+    i = p.info()
+    assert (i.tile_id, i.bm, i.bn, i.bk, i.waves, i.stages) == (1, 256, 256, 64, 4, 2)
+    assert i.lds_bytes == 2 * (256 * 64 + 64 * 256) * 2 == 131072
+    assert (i.tiles_m, i.tiles_n, i.workgroups, i.trips) == (16, 16, 256, 64)
+    # MFMA count: tiles * (256/32)^2 blocks * trips * (64/16) k-steps
+    assert i.mfma_per_run == 256 * 64 * 64 * 4 == 4194304
+    assert i.vec16 == 1
+    assert "stages 2" in p.describe()
+
+
+def test_stage_fallbacks_follow_lds_budget():
+    assert plan(4096, 4096, 4096, tile=1, caps=tcg.make_caps(lds_bytes=100 * 1024)).info().stages == 1
+    assert plan(4096, 4096, 4096, tile=1, caps=tcg.make_caps(lds_bytes=40 * 1024)).info().stages == 0
+    assert plan(4096, 4096, 4096, tile=1, caps=tcg.make_caps(async_copy=0)).info().stages == 1
+    assert plan(4096, 4096, 4096, flags=tcg.FLAG_FORCE_STAGES_1).info().stages == 1
+    p = plan(4096, 4096, 4096, flags=tcg.FLAG_UNSTAGED)
+    assert p.info().stages == 0 and p.info().lds_bytes == 0
+
+
+def test_short_k_token_projection_takes_wide_tile():
+    i = plan(129600, 288, 96, F16, F16, EPI_NONE).info()
+    assert i.bn == 288 and i.tiles_n == 1 and i.trips == 3
+
+
+def test_ragged_and_small_shapes_fill_the_chip():
+    i = plan(1000, 1000, 1000, F16, F32).info()
+    assert i.workgroups >= 200
+    i = plan(2048, 2048, 16384, BF16, BF16, EPI_NONE).info()
+    assert i.workgroups >= 256
+
+
+def test_vec16_needs_aligned_rows():
+    assert plan(100, 64, 24).info().vec16 == 1
+    assert plan(100, 64, 13).info().vec16 == 0
+    assert plan(100, 60, 24).info().vec16 == 0
+    assert plan(10, 16, 16, batch=2, sa=164, sb=256, sc=160).info().vec16 == 0
+
+
+def test_invalid_descriptions():
+    cases = [
+        (dict(M=-1, N=4, K=4), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=-1), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, batch=0), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, in_dtype=F32), tcg.GEMM_E_DTYPE),
+        (dict(M=4, N=4, K=4, out_dtype=9), tcg.GEMM_E_DTYPE),
+        (dict(M=4, N=4, K=4, epi=7), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, flags=8), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, tile=99), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, batch=2, sa=15, sb=16, sc=16), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=2**31), tcg.GEMM_E_SIZE),
+    ]
+    for kw, code in cases:
+        with pytest.raises(tcg.GemmError) as e:
+            plan(**kw)
+        assert e.value.code == code, kw
+    with pytest.raises(tcg.GemmError) as e:
+        tcg.gemm_plan_for_caps(tcg.make_desc(4, 4, 4), tcg.make_caps(wave_size=32))
+    assert e.value.code == tcg.GEMM_E_DEVICE
+
+
+def test_degenerate_sizes_plan():
+    assert plan(0, 5, 5).info().workgroups == 0
+    i = plan(5, 5, 0).info()
+    assert i.trips == 0 and i.mfma_per_run == 0
+
+
+def test_every_tile_id_plans():
+    for t in range(1, tcg.gemm_tile_count() + 1):
+        i = plan(1000, 1000, 1000, tile=t).info()
+        assert i.tile_id == t and i.stages == 2
+        assert i.lds_bytes <= 163840
+
+
+def test_null_plan_is_rejected():
+    fake = tcg.Plan.__new__(tcg.Plan)
+    fake._h = tcg.capi._vp(None)
+    fake.desc = None
+    with pytest.raises(tcg.GemmError) as e:
+        tcg.gemm_plan_get_info(fake)
+    assert e.value.code == tcg.GEMM_E_PLAN
+    with pytest.raises(tcg.GemmError) as e:
+        tcg.gemm_run(fake, 0, 0, 0, stream=0)
+    assert e.value.code == tcg.GEMM_E_PLAN
+
+
+def test_gemm_plan_without_a_device_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    with pytest.raises(tcg.GemmError) as e:
+        tcg.gemm_plan(tcg.make_desc(64, 64, 64))
+    assert e.value.code == tcg.GEMM_E_DEVICE

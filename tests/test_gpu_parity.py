@@ -1,0 +1,209 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+Bars: bit-exact on integer inputs; max relative error <= 1e-2 (floor at
+0.01 of an output's standard deviation) on Gaussian/uniform inputs; the
+staged kernels equal the unstaged kernel bit for bit (page "Module
+Tolk.Stage": staging moves values and never rounds them); one stage equals
+two stages; repeat runs are identical; nothing outside C's M x N region is
+written (page "gizml:tile", Out.put / Program.write).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gemm_workloads as gw
+from gemm_workloads import BF16, EPI_NONE, EPI_RELU, F16, F32
+from gpu_helpers import as_bits, as_values, check_against_oracle, check_sampled, note, run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tcg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_core_gemm_amd as t
+    t.check_runtime()
+    caps = t.gemm_device_caps_query(0)
+    note(f"device: {caps.arch.decode()} CUs={caps.num_cus} LDS/WG={caps.lds_bytes} "
+         f"clock={caps.clock_khz} kHz")
+    return t
+
+
+W = gw.WORKLOADS
+SMALL = ["int_fp16_256", "ragged_fp16_1000"]
+BIG = ["bf16_4096_relu", "swin_proj_fp16", "deepk_bf16_2048x16384"]
+
+# The large workloads' dtype, epilogue and input recipe at sizes the oracle
+# computes in full within seconds, each spanning several tiles and a ragged tail.
+SCALED = {
+    "bf16_4096_relu": gw.custom(600, 520, 700, BF16, BF16, EPI_RELU, gw.NORMAL, seed=21,
+                                name="bf16_relu_600x520x700"),
+    "swin_proj_fp16": gw.custom(3000, 288, 96, F16, F16, EPI_NONE, gw.NORMAL, seed=31,
+                                dist_b=gw.Dist("normal", 0.0, 96 ** -0.5), name="swin_3000"),
+    "deepk_bf16_2048x16384": gw.custom(300, 260, 4000, BF16, BF16, EPI_NONE, gw.NORMAL, seed=51,
+                                       name="deepk_300x260x4000"),
+}
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_workloads_full(tcg, name):
+    w = W[name]
+    A, B = gw.make_inputs(w)
+    C, _, _ = run(tcg, A, B, w)
+    check_against_oracle(w, A, B, C)
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_scaled_workloads_full(tcg, name):
+    w = SCALED[name]
+    A, B = gw.make_inputs(w)
+    C, _, _ = run(tcg, A, B, w)
+    check_against_oracle(w, A, B, C)
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_full_size_sampled(tcg, name):
+    """Full size, the planner's launch configuration (the one the benchmark
+    times), 4096 sampled outputs checked one by one."""
+    w = W[name]
+    A, B = gw.make_inputs(w)
+    C, _, _ = run(tcg, A, B, w)
+    assert np.all(np.isfinite(as_values(C)))
+    check_sampled(w, A, B, C)
+
+
+@pytest.mark.parametrize("name", list(W))
+def test_staged_equals_unstaged_bitwise(tcg, name):
+    w = W[name]
+    A, B = gw.make_inputs(w)
+    Cs, _, ps = run(tcg, A, B, w)
+    tile = ps.info().tile_id
+    Cu, _, pu = run(tcg, A, B, w, flags=tcg.FLAG_UNSTAGED, tile=tile)
+    assert pu.info().stages == 0 and ps.info().stages > 0
+    assert np.array_equal(as_bits(Cs), as_bits(Cu))
+
+
+@pytest.mark.parametrize("name", list(W))
+def test_one_stage_equals_two_stages_bitwise(tcg, name):
+    w = W[name]
+    A, B = gw.make_inputs(w)
+    C2, _, p2 = run(tcg, A, B, w)
+    C1, _, p1 = run(tcg, A, B, w, flags=tcg.FLAG_FORCE_STAGES_1, tile=p2.info().tile_id)
+    assert p2.info().stages == 2 and p1.info().stages == 1
+    assert np.array_equal(as_bits(C1), as_bits(C2))
+
+
+def test_repeat_runs_identical(tcg):
+    w = W["ragged_fp16_1000"]
+    A, B = gw.make_inputs(w)
+    first = as_bits(run(tcg, A, B, w)[0])
+    for _ in range(3):
+        assert np.array_equal(as_bits(run(tcg, A, B, w)[0]), first)
+
+
+@pytest.mark.parametrize("out_dtype", [F32, F16, BF16])
+def test_guard_band_untouched(tcg, out_dtype):
+    w = gw.custom(333, 250, 190, F16, out_dtype, EPI_RELU, gw.UNIT, seed=7)
+    A, B = gw.make_inputs(w)
+    guard = 4096
+    sentinel = 0x5A5A5A5A if out_dtype == F32 else 0x5A5A
+    C, buf, _ = run(tcg, A, B, w, guard=guard, sentinel=sentinel)
+    raw = as_bits(buf)
+    sent = np.array(sentinel, raw.dtype)
+    assert np.all(raw[:guard] == sent) and np.all(raw[-guard:] == sent)
+    check_against_oracle(w, A, B, C)
+
+
+def test_batch_strides(tcg):
+    w = gw.custom(130, 70, 90, BF16, F32, EPI_RELU, gw.NORMAL, seed=9, batch=3)
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w)
+    assert p.info().workgroups == p.info().tiles_m * p.info().tiles_n * 3
+    check_against_oracle(w, A, B, C)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+def test_every_tile_gives_the_exact_integer_result(tcg, tile):
+    """Every tile configuration computes the same result (page "gizml:tile",
+    tune: every configuration must compute the same result)."""
+    w = gw.custom(300, 288, 300, F16, F32, EPI_NONE, gw.INT4, seed=11)
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w, tile=tile)
+    assert p.info().tile_id == tile
+    check_against_oracle(w, A, B, C)
+
+
+EDGE = [(1, 1, 1), (1, 300, 17), (300, 1, 64), (33, 65, 16), (64, 64, 64), (257, 255, 129),
+        (17, 513, 1000), (96, 96, 8)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+@pytest.mark.parametrize("in_dtype,out_dtype", [(F16, F32), (BF16, BF16), (F16, F16)])
+def test_edge_shapes(tcg, M, N, K, in_dtype, out_dtype):
+    for dist in (gw.INT4, gw.NORMAL):
+        w = gw.custom(M, N, K, in_dtype, out_dtype, EPI_RELU, dist, seed=M + N + K)
+        A, B = gw.make_inputs(w)
+        C, _, _ = run(tcg, A, B, w)
+        check_against_oracle(w, A, B, C)
+
+
+def test_k_zero_writes_positive_zero(tcg):
+    for out_dtype in (F32, F16, BF16):
+        w = gw.custom(70, 90, 0, BF16, out_dtype, EPI_NONE, gw.NORMAL)
+        A = torch.zeros(0, dtype=torch.bfloat16)
+        B = torch.zeros(0, dtype=torch.bfloat16)
+        C, _, _ = run(tcg, A, B, w, sentinel=0x1234)
+        assert np.all(as_bits(C) == 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(45, 21, 13), (130, 77, 250), (64, 100, 9)])
+def test_element_copy_path(tcg, M, N, K):
+    """K or N not a multiple of 8: rows are not 16-byte aligned, so the
+    element-copy kernels run; compared with the oracle and the unstaged kernel."""
+    w = gw.custom(M, N, K, F16, F32, EPI_RELU, gw.NORMAL, seed=K)
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w)
+    assert p.info().vec16 == 0
+    check_against_oracle(w, A, B, C)
+    Cu, _, _ = run(tcg, A, B, w, flags=tcg.FLAG_UNSTAGED, tile=p.info().tile_id)
+    assert np.array_equal(as_bits(C), as_bits(Cu))
+
+
+def test_misaligned_pointers_take_the_element_path(tcg):
+    w = gw.custom(200, 136, 128, BF16, BF16, EPI_RELU, gw.NORMAL, seed=3)
+    A, B = gw.make_inputs(w)
+    C0, _, p = run(tcg, A, B, w)
+    C1, _, _ = run(tcg, A, B, w, plan=p, a_offset=1, b_offset=3)
+    assert np.array_equal(as_bits(C0), as_bits(C1))
+    check_against_oracle(w, A, B, C0)
+
+
+def test_lds_budget_fallbacks_give_the_same_bits(tcg):
+    """The stage rule (page "Module Tolk.Stage", depth): with less LDS the
+    planner takes one stage, then none; every plan returns the same bits."""
+    w = gw.custom(512, 512, 512, BF16, BF16, EPI_RELU, gw.NORMAL, seed=5)
+    A, B = gw.make_inputs(w)
+    desc = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, tile=1)
+    results = []
+    for lds, want in ((163840, 2), (100 * 1024, 1), (40 * 1024, 0)):
+        p = tcg.gemm_plan_for_caps(desc, tcg.make_caps(lds_bytes=lds))
+        assert p.info().stages == want
+        results.append(as_bits(run(tcg, A, B, w, plan=p)[0]))
+    assert np.array_equal(results[0], results[1]) and np.array_equal(results[0], results[2])
+
+
+def test_run_errors(tcg):
+    w = gw.custom(64, 64, 64, F16, F16, EPI_NONE, gw.NORMAL)
+    p = tcg.gemm_plan(tcg.make_desc(64, 64, 64, F16, F16))
+    buf = torch.zeros(3 * 64 * 64, dtype=torch.float16, device="cuda")
+    A, B = buf[:4096], buf[4096:8192]
+    with pytest.raises(tcg.GemmError) as e:
+        tcg.gemm_run(p, A, B, buf[2048:6144])  # C overlaps A and B
+    assert e.value.code == tcg.GEMM_E_ALIAS
+    with pytest.raises(tcg.GemmError) as e:
+        tcg.gemm_run(p, A, B, 0)
+    assert e.value.code == tcg.GEMM_E_ARG
+    tcg.gemm_run(p, A, B, buf[8192:])  # disjoint: fine
+    torch.cuda.synchronize()
+    del w

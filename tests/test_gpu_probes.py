@@ -1,0 +1,147 @@
+"""Hardware lane layouts the GEMM kernels rely on, measured on gfx950.
+
+The fragment loaders assume (a) MFMA operand/result lane layouts, (b) the
+lane permutation of the transposing LDS read ds_read_b64_tr_b16 and (c) the
+LDS placement and out-of-range zero-fill of a buffer load that writes LDS
+directly.  Each test runs one small in-bounds probe kernel and checks the
+assumption; on a mismatch it prints what the hardware did.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+OUT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+
+
+def _record(name, obj):
+    if os.path.isdir(OUT_DIR):
+        with open(os.path.join(OUT_DIR, f"probe_{name}.json"), "w") as f:
+            json.dump(obj, f)
+
+
+@pytest.fixture(scope="module")
+def probe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tensor_core_gemm_amd import probe as p
+    return p
+
+
+def _bits(x, bf16):
+    t = torch.tensor(np.asarray(x, np.float32))
+    t = t.to(torch.bfloat16 if bf16 else torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_mfma_32x32x16_layout(probe, kind):
+    """A lane l: row l%32, k 8*(l//32)+e; B lane l: col l%32, same k;
+    D lane l, register r: row 8*(r//4) + 4*(l//32) + r%4, col l%32."""
+    rng = np.random.default_rng(kind)
+    A = rng.integers(-4, 5, (32, 16)).astype(np.float32)
+    B = rng.integers(-4, 5, (16, 32)).astype(np.float32)
+    bf16 = kind == 0
+    a_regs = np.zeros((64, 8), np.float32)
+    b_regs = np.zeros((64, 8), np.float32)
+    for l in range(64):
+        for e in range(8):
+            a_regs[l, e] = A[l % 32, 8 * (l // 32) + e]
+            b_regs[l, e] = B[8 * (l // 32) + e, l % 32]
+    d = probe.mfma(kind, _bits(a_regs, bf16), _bits(b_regs, bf16))
+    ref = A @ B
+    want = np.zeros((64, 16), np.float32)
+    for l in range(64):
+        for r in range(16):
+            want[l, r] = ref[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32]
+    if not np.array_equal(d, want):
+        _record(f"mfma32_{kind}", {"A": A.tolist(), "B": B.tolist(), "d": d.tolist()})
+    assert np.array_equal(d, want)
+
+
+@pytest.mark.parametrize("kind", [2, 3])
+def test_mfma_16x16x32_layout(probe, kind):
+    """A lane l: row l%16, k 8*(l//16)+e; D lane l, register r: row
+    4*(l//16) + r, col l%16."""
+    rng = np.random.default_rng(kind)
+    A = rng.integers(-4, 5, (16, 32)).astype(np.float32)
+    B = rng.integers(-4, 5, (32, 16)).astype(np.float32)
+    bf16 = kind == 2
+    a_regs = np.zeros((64, 8), np.float32)
+    b_regs = np.zeros((64, 8), np.float32)
+    for l in range(64):
+        for e in range(8):
+            a_regs[l, e] = A[l % 16, 8 * (l // 16) + e]
+            b_regs[l, e] = B[8 * (l // 16) + e, l % 16]
+    d = probe.mfma(kind, _bits(a_regs, bf16), _bits(b_regs, bf16))
+    ref = A @ B
+    want = np.zeros((64, 16), np.float32)
+    for l in range(64):
+        for r in range(4):
+            want[l, r] = ref[4 * (l // 16) + r, l % 16]
+    if not np.array_equal(d, want):
+        _record(f"mfma16_{kind}", {"A": A.tolist(), "B": B.tolist(), "d": d.tolist()})
+    assert np.array_equal(d, want)
+
+
+def test_ds_read_tr16_permutation(probe):
+    """Lane l reads 4 16-bit values at byte l*8 (value = element index), so
+    source (lane s, element e) carries 4*s + e.  Measured on gfx950: within
+    each group of 16 lanes, dst(lane x, element e) = src(lane 4*e + x//4,
+    element x%4); the B-fragment loader's addresses are derived from it."""
+    init = np.arange(4096, dtype=np.uint16)
+    addr = np.arange(64, dtype=np.uint32) * 8
+    out = probe.ds_read_tr16(init, addr)
+    src_lane, src_elem = out // 4, out % 4
+    _record("tr16", {"out": out.tolist()})
+    print("dst -> (src lane, src elem):")
+    for j in range(64):
+        print(j, list(zip(src_lane[j].tolist(), src_elem[j].tolist())))
+    want = np.zeros((64, 4), np.int64)
+    for j in range(64):
+        for e in range(4):
+            g, x = 16 * (j // 16), j % 16
+            want[j, e] = 4 * (g + 4 * e + x // 4) + x % 4
+    assert np.array_equal(out.astype(np.int64), want)
+
+
+def test_buffer_lds_placement_and_zero_fill(probe):
+    """Lane l's 16 bytes land at LDS base + 16*l; offsets at or past
+    num_records read 0 (the source allocation is twice num_records, so the
+    out-of-range offsets used here still point at owned memory)."""
+    words = 4096
+    src = torch.arange(words, dtype=torch.int32, device="cuda") + 1000
+    records = 8192  # bytes: half the allocation
+    voff = np.array([((l * 37) % 64) * 16 for l in range(64)], np.uint32)
+    oob = np.arange(56, 64)
+    voff[oob] = 8192 + 16 * np.arange(8)  # past num_records, inside the allocation
+    base = 1024
+    lds = probe.buffer_lds(src, records, voff, base)
+    want = np.full(2048, 0xDEADBEEF, np.uint64)
+    for l in range(64):
+        for w in range(4):
+            v = 0 if l in oob else 1000 + voff[l] // 4 + w
+            want[base // 4 + 4 * l + w] = v
+    if not np.array_equal(lds.astype(np.uint64), want):
+        _record("buffer_lds", {"lds": lds.tolist(), "voff": voff.tolist()})
+    assert np.array_equal(lds.astype(np.uint64), want)
+
+
+def test_buffer_lds_high_offset_reads_zero(probe):
+    """The kernels mark masked lanes with byte offset 0x80000000; the same
+    range check as above must turn it into a zero read."""
+    src = torch.arange(4096, dtype=torch.int32, device="cuda") + 1000
+    voff = np.array([16 * l for l in range(64)], np.uint32)
+    voff[5] = 0x80000000
+    voff[63] = 0x80000000
+    lds = probe.buffer_lds(src, 8192, voff, 0)
+    got = lds[:256].reshape(64, 4)
+    for l in range(64):
+        if l in (5, 63):
+            assert np.all(got[l] == 0)
+        else:
+            assert np.array_equal(got[l], 1000 + 4 * l + np.arange(4))
