@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of C = epilogue(A . B) on one MI355X: prints one JSON line.
+
+A step is one gemm_run of the workload over inputs already resident in HBM.
+Default workload: bf16 M = N = K = 4096, A, B ~ N(0, 1), relu, bf16 out
+(the headline GEMM).  W untimed warm-up steps, then K timed steps between
+two device synchronisations; the average launch duration of the kernel is
+measured with HIP events recorded on the stream the kernel is launched on.
+
+roofline: the kernel is bound by the MFMA units; achieved = 2*M*N*K flops
+per launch / average launch duration, against MI355X's published dense
+fp16/bf16 MFMA peak (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 flop/CU/clk).
+
+cpu_baseline: the CPU oracle (plain C, fp32, OpenMP) timed on this host's
+cores on a bounded sample of the same workload: the first r rows of C
+(r x N x K multiply-adds), r chosen so the oracle works about 10-20 s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = {4: 2516.6, 5: 2516.6}  # dense fp16 / bf16, MI355X
+PEAK_HBM_GBS = 8000.0
+METRIC = "GEMM TFLOP/s and % of MI355X dense MFMA peak (bf16 4096^3)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_4096_relu")
+    ap.add_argument("--tile", type=int, default=0, help="force a tile configuration id")
+    ap.add_argument("--flags", type=int, default=0, help="plan flags (1: one stage, 2: unstaged)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--rotate", type=int, default=1,
+                    help="input/output sets cycled between steps (>1 defeats cache reuse)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before the GEMM, run a plain device copy of this many MiB three "
+                         "times (a known-size reference for the HBM byte counters)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the GEMM would shard along M or N with no exchange step).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gemm_workloads as gw
+    import tensor_core_gemm_amd as tcg
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    tcg.check_runtime()
+    w = gw.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    caps = tcg.gemm_device_caps_query(0)
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    A_cpu, B_cpu = gw.make_inputs(w)
+    sets = []
+    for r in range(max(args.rotate, 1)):
+        A = A_cpu.to(dev) if r == 0 else A_cpu.to(dev).clone()
+        B = B_cpu.to(dev) if r == 0 else B_cpu.to(dev).clone()
+        C = torch.empty((w.M, w.N), dtype=gw.TORCH_DTYPE[w.out_dtype], device=dev)
+        sets.append((A, B, C))
+    desc = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, args.flags,
+                         tile=args.tile)
+    plan = tcg.gemm_plan(desc)
+    info = plan.info()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        A, B, C = sets[i % len(sets)]
+        tcg.gemm_run(plan, A, B, C, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    durs_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    avg_launch_ms = sum(durs_ms) / K
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[w.in_dtype]
+
+    # quick sanity check of the timed output against the oracle (64 samples)
+    import numpy as np
+
+    import oracle
+    bi, ii, jj = gw.sample_indices(w.M, w.N, 64, 99)
+    _, y = oracle.gemm_sampled(A_cpu, B_cpu, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
+                               bi, ii, jj)
+    got = sets[(K - 1) % len(sets)][2].float().cpu().numpy()[ii, jj]
+    s = w.sigma_out()
+    sample_err = float(np.max(np.abs(got - y) / np.maximum(np.abs(y), 0.01 * s)))
+
+    traffic = None
+    try:
+        with open(args.traffic) as f:
+            t = json.load(f).get(w.name)
+        if t and t.get("kernel_source_sha") == kernel_source_sha():
+            traffic = t["hbm_bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.in_dtype == gw.BF16 else "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+            "in": gw.DTYPE_NAME[w.in_dtype], "out": gw.DTYPE_NAME[w.out_dtype],
+            "epilogue": "relu" if w.epilogue else "none", "accumulate": "f32",
+            "plan": plan.describe(), "pct_of_peak": round(100 * value / peak, 2),
+            "device": caps.arch.decode(), "cus": caps.num_cus, "clock_mhz": caps.clock_khz // 1000,
+            "sample_max_rel_err": sample_err,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel_avg_ms": round(avg_launch_ms, 5),
+            "flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, A_cpu, B_cpu, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def kernel_source_sha() -> str:
+    """Hash of the kernel sources, so stale counter data is not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tensor_core_gemm_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(csrc, fn), "rb") as f:
+                h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, A, B, target_s):
+    """The oracle as it is, on this host's cores, over the first r rows."""
+    import oracle
+    threads = oracle.threads()
+    a = A.reshape(w.M, w.K)
+    rows = max(1, min(w.M, 16))
+    t0 = time.perf_counter()
+    oracle.gemm(a[:rows].contiguous(), B, rows, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue)
+    dt = time.perf_counter() - t0
+    # scale to the target time, then measure that sample
+    rows = int(max(1, min(w.M, rows * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.gemm(a[:rows].contiguous(), B, rows, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.M} rows of C ({rows}x{w.N}x{w.K}, "
+                  f"{flops / 1e9:.1f} GFLOP) in {dt:.2f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

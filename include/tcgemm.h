@@ -50,8 +50,10 @@ enum { GEMM_EPI_NONE = 0, GEMM_EPI_RELU = 1 };
  *   GEMM_FLAG_FORCE_STAGES_1: use at most one LDS stage even where two fit.
  *   GEMM_FLAG_UNSTAGED: no LDS staging; fragments are loaded straight from
  *     global memory (the "Setting.stage off" case of the page "Module
- *     Tolk.Stage", depth). */
-enum { GEMM_FLAG_FORCE_STAGES_1 = 1, GEMM_FLAG_UNSTAGED = 2 };
+ *     Tolk.Stage", depth).
+ *   GEMM_FLAG_FORCE_STAGES_2: use at most two stages even where the tile's
+ *     kernel could keep more chunks in flight. */
+enum { GEMM_FLAG_FORCE_STAGES_1 = 1, GEMM_FLAG_UNSTAGED = 2, GEMM_FLAG_FORCE_STAGES_2 = 4 };
 
 /* Error codes. */
 enum {
@@ -101,7 +103,7 @@ typedef struct gemm_plan_info {
   int32_t tile_id;
   int32_t bm, bn, bk;       /* workgroup tile                                */
   int32_t waves;            /* waves (64 lanes) per workgroup                */
-  int32_t stages;           /* 2, 1, or 0 (unstaged)                         */
+  int32_t stages;           /* LDS slots in the ring (2..4), 1, or 0 (unstaged) */
   int32_t lds_bytes;        /* LDS the kernel declares                       */
   int32_t vec16;            /* 1: 16-byte copies; 0: element copies          */
   int64_t tiles_m, tiles_n; /* output tiles along M and N                    */

@@ -10,7 +10,8 @@ from __future__ import annotations
 
 import torch
 
-from .capi import (BF16, EPI_NONE, EPI_RELU, F16, F32, FLAG_FORCE_STAGES_1, FLAG_UNSTAGED,
+from .capi import (BF16, EPI_NONE, EPI_RELU, F16, F32, FLAG_FORCE_STAGES_1, FLAG_FORCE_STAGES_2,
+                   FLAG_UNSTAGED,
                    GEMM_E_ALIAS, GEMM_E_ALIGN, GEMM_E_ARG, GEMM_E_DEVICE, GEMM_E_DTYPE,
                    GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE, GEMM_OK, CODE_TO_TORCH,
                    TORCH_TO_CODE, GemmError, Plan, check_runtime, gemm_desc, gemm_device_caps,

@@ -15,7 +15,7 @@ from ._lib import lib
 
 F32, F16, BF16 = 0, 4, 5
 EPI_NONE, EPI_RELU = 0, 1
-FLAG_FORCE_STAGES_1, FLAG_UNSTAGED = 1, 2
+FLAG_FORCE_STAGES_1, FLAG_UNSTAGED, FLAG_FORCE_STAGES_2 = 1, 2, 4
 
 GEMM_OK = 0
 GEMM_E_ARG, GEMM_E_DTYPE, GEMM_E_ALIGN, GEMM_E_ALIAS = -1, -2, -3, -4

@@ -68,7 +68,7 @@ int validate_desc(const gemm_desc* d) {
   if (d->out_dtype != GEMM_F32 && d->out_dtype != GEMM_F16 && d->out_dtype != GEMM_BF16)
     return GEMM_E_DTYPE;
   if (d->epilogue != GEMM_EPI_NONE && d->epilogue != GEMM_EPI_RELU) return GEMM_E_ARG;
-  if (d->flags & ~(GEMM_FLAG_FORCE_STAGES_1 | GEMM_FLAG_UNSTAGED)) return GEMM_E_ARG;
+  if (d->flags & ~(GEMM_FLAG_FORCE_STAGES_1 | GEMM_FLAG_UNSTAGED | GEMM_FLAG_FORCE_STAGES_2)) return GEMM_E_ARG;
   if (d->tile < 0 || d->tile > tcg::kNumTiles) return GEMM_E_ARG;
   if (d->reserved != 0) return GEMM_E_ARG;
   if (d->batch > 1) {
@@ -212,6 +212,13 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
 
   const int64_t tiles[2] = {(int64_t)t.bm * t.bk * 2, (int64_t)t.bk * t.bn * 2};
   int stages = gemm_stage_depth(caps, 0, tiles, 2, (d.flags & GEMM_FLAG_UNSTAGED) ? 0 : 1);
+  // Where two stages fit and the tile's kernel is built for a deeper ring,
+  // keep more chunks in flight while they fit: more stages hide longer
+  // memory latency at the cost of LDS (page "gizml:tile", Program.stages).
+  if (stages == 2 && t.max_stages > 2 && !(d.flags & GEMM_FLAG_FORCE_STAGES_2)) {
+    const int64_t fit = (int64_t)caps->lds_bytes / (tiles[0] + tiles[1]);
+    stages = (int)std::min<int64_t>(t.max_stages, fit);
+  }
   if ((d.flags & GEMM_FLAG_FORCE_STAGES_1) && stages > 1) stages = 1;
 
   // Byte offsets inside one trip's tiles are 32-bit buffer offsets.
@@ -363,6 +370,8 @@ extern "C" int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
     case 3: e = tcg::launch_t3(in.stages, vec16, bf16, a, s); break;
     case 4: e = tcg::launch_t4(in.stages, vec16, bf16, a, s); break;
     case 5: e = tcg::launch_t5(in.stages, vec16, bf16, a, s); break;
+    case 6: e = tcg::launch_t6(in.stages, vec16, bf16, a, s); break;
+    case 7: e = tcg::launch_t7(in.stages, vec16, bf16, a, s); break;
     default: break;
   }
   if (e != hipSuccess) {

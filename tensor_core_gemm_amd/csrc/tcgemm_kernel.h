@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tcgemm_kernel_args.h"
 #include "tcgemm_tiles.h"
 
@@ -64,6 +66,22 @@ __device__ __forceinline__ int swz_b(int r) {
   // rows 4q .. 4q+3 are XORed with 0, 6, 10, 12 (reduced to the row's mask)
   const int t = (0xCA60 >> (4 * (r & 3))) & 15;
   return t & swizzle_mask(CPR);
+}
+
+// ---------------------------------------------------------------------------
+// s_waitcnt immediate (gfx9 encoding): vmcnt = N (bits 3:0 and 15:14),
+// expcnt unchanged (7), lgkmcnt = 0.
+template <int N>
+constexpr int waitcnt_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4);
+}
+
+// A workgroup barrier.  The waits it needs are issued explicitly before it
+// (the waitcnt above); the memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void workgroup_barrier() {
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -320,7 +338,9 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     // ---------------- staged through LDS ----------------------------------
     // slot0 also holds the epilogue's output bands after the last trip.
     __shared__ __attribute__((aligned(1024))) char slot0[T::SLOT > T::EPI_BYTES ? T::SLOT : T::EPI_BYTES];
-    __shared__ __attribute__((aligned(1024))) char slot1[STAGES == 2 ? T::SLOT : 16];
+    __shared__ __attribute__((aligned(1024))) char slot1[STAGES >= 2 ? T::SLOT : 16];
+    __shared__ __attribute__((aligned(1024))) char slot2[STAGES >= 3 ? T::SLOT : 16];
+    __shared__ __attribute__((aligned(1024))) char slot3[STAGES >= 4 ? T::SLOT : 16];
     smem_epi = slot0;
 
     // Copy plan.  Lane position P = i*NT + tid of a slot's chunk array holds
@@ -471,22 +491,55 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma<BF16IN>(f.b[j], f.a[i], acc[i][j]);
     };
     auto wait_all_and_barrier = [&]() __attribute__((always_inline)) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+      workgroup_barrier();
     };
 
     Frags f0, f1;
-    if constexpr (STAGES == 2) {
-      // Trip t reads slot t mod 2 while chunk t+1 lands in the other slot.
+    if constexpr (STAGES >= 2) {
+      // A ring of S slots.  Trip t reads slot t mod S while chunks t+1 ..
+      // t+S-1 are in flight into the other slots; at its start it issues the
+      // copy of chunk t+S-1 into slot (t-1) mod S, the slot trip t-1 read.
+      // With S = 2 this is the two-stage pipeline of the page "Module
+      // Tolk.Stage"; more stages hide longer memory latency at the cost of
+      // LDS (page "gizml:tile", Program.stages).
+      //
       // The one barrier of a trip comes after the last k-step's fragments
-      // are in registers and this wave's copy has landed: it retires every
-      // read of slot t mod 2 before trip t+1 overwrites it, and publishes
-      // chunk t+1 before it is read.  The last k-step's MFMAs then run while
-      // the first fragments of chunk t+1 load.
-      auto trip = [&](int t, char* cur, char* nxt) __attribute__((always_inline)) {
+      // are in registers and this wave's copy of chunk t+1 has landed: it
+      // retires every read of slot t mod S before trip t+1 overwrites it
+      // (with chunk t+S), and publishes chunk t+1 before it is read.  The
+      // last k-step's MFMAs then run while the first fragments of chunk t+1
+      // load.  Vector-memory loads complete in order, so "chunk t+1 has
+      // landed" is a wait until at most the copies of the newer chunks
+      // (t+2 .. t+S-1, NDMA instructions each) are outstanding.
+      constexpr int S = STAGES;
+      static_assert(S == 2 || (T::CH_A % NT == 0 && T::CH_B % NT == 0),
+                    "rings deeper than two need whole copy rounds per wave");
+      constexpr int NDMA = T::IA + T::IB;  // copy instructions per wave per chunk
+      char* const ring[4] = {slot0, slot1, slot2, slot3};
+      auto wait_newer_and_barrier = [&](int newer) __attribute__((always_inline)) {
+        // newer: copies of chunks after the awaited one still allowed in flight
+        if constexpr (S >= 4) {
+          if (newer >= 2) { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<2 * NDMA>()); }
+          else if (newer == 1) { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NDMA>()); }
+          else { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>()); }
+        } else if constexpr (S == 3) {
+          if (newer >= 1) { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NDMA>()); }
+          else { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>()); }
+        } else {
+          (void)newer;
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+        }
+        workgroup_barrier();
+      };
+      auto trip = [&](int t, auto J) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value;
+        char* cur = ring[j];
+        char* cp = ring[(j + S - 1) % S];
+        char* nxt = ring[(j + 1) % S];
         // The copy is issued first and kept there: the scheduler may not
         // sink it towards the barrier, where it would no longer overlap.
-        if (t + 1 < trips) copy(t + 1, nxt);
+        if (t + S - 1 < trips) copy(t + S - 1, cp);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -496,7 +549,8 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
             load(cur, s + 1, next);
             mma(now);
           } else {
-            wait_all_and_barrier();
+            const int issued_after = (t + S - 1 < trips ? t + S - 1 : trips - 1) - (t + 1);
+            wait_newer_and_barrier(issued_after > 0 ? issued_after : 0);
             if (t + 1 < trips) load(nxt, 0, next);
             mma(now);
           }
@@ -504,20 +558,35 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
         }
       };
       if (trips > 0) {
-        copy(0, slot0);
-        wait_all_and_barrier();
+#pragma unroll
+        for (int c = 0; c < S - 1; ++c)
+          if (c < trips) copy(c, ring[c]);
+        const int issued_after = (S - 2 < trips - 1 ? S - 2 : trips - 1);
+        wait_newer_and_barrier(issued_after > 0 ? issued_after : 0);
         load(slot0, 0, f0);
       }
-      // Unrolled by two so that each copy and each read names one slot;
-      // an odd last trip is peeled so the loop body has no branch around a
-      // whole trip.  KS is even, so every trip starts with its fragments in f0.
+      // Unrolled by S so that each copy and each read names one slot; the
+      // last trips are peeled so the loop body has no branch around a whole
+      // trip.  KS is even, so every trip starts with its fragments in f0.
       static_assert(KS % 2 == 0, "k-steps per trip must be even");
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
       int t = 0;
-      for (; t + 1 < trips; t += 2) {
-        trip(t, slot0, slot1);
-        trip(t + 1, slot1, slot0);
+      for (; t + S <= trips; t += S) {
+        trip(t, I0{});
+        trip(t + 1, I1{});
+        if constexpr (S >= 3) trip(t + 2, I2{});
+        if constexpr (S >= 4) trip(t + 3, I3{});
       }
-      if (t < trips) trip(t, slot0, slot1);
+      if (t < trips) trip(t, I0{});
+      if constexpr (S >= 3) {
+        if (t + 1 < trips) trip(t + 1, I1{});
+      }
+      if constexpr (S >= 4) {
+        if (t + 2 < trips) trip(t + 2, I2{});
+      }
     } else {
       for (int t = 0; t < trips; ++t) {
         copy(t, slot0);
@@ -530,7 +599,7 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
           if (s + 1 < KS) load(slot0, s + 1, next);
           mma(now);
         }
-        __syncthreads();  // retires the reads before the next copy
+        wait_all_and_barrier();  // retires the reads before the next copy
       }
     }
   }
@@ -555,11 +624,18 @@ hipError_t launch_one(const KArgs& a, hipStream_t stream) {
 
 template <int TID>
 hipError_t launch_tile(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s) {
-#define TCG_CASE(ST, V, BF) \
-  if (stages == ST && vec16 == V && bf16 == BF) return launch_one<TID, ST, V, BF>(a, s);
-  TCG_CASE(2, true, true) TCG_CASE(2, true, false) TCG_CASE(2, false, true) TCG_CASE(2, false, false)
-  TCG_CASE(1, true, true) TCG_CASE(1, true, false) TCG_CASE(1, false, true) TCG_CASE(1, false, false)
-  TCG_CASE(0, true, true) TCG_CASE(0, true, false) TCG_CASE(0, false, true) TCG_CASE(0, false, false)
+#define TCG_CASE(ST)                                                            \
+  if (stages == ST) {                                                           \
+    if (vec16) return bf16 ? launch_one<TID, ST, true, true>(a, s)              \
+                           : launch_one<TID, ST, true, false>(a, s);            \
+    return bf16 ? launch_one<TID, ST, false, true>(a, s)                        \
+                : launch_one<TID, ST, false, false>(a, s);                      \
+  }
+  TCG_CASE(0)
+  TCG_CASE(1)
+  TCG_CASE(2)
+  if constexpr (Tile<TID>::MAX_STAGES >= 3) { TCG_CASE(3) }
+  if constexpr (Tile<TID>::MAX_STAGES >= 4) { TCG_CASE(4) }
 #undef TCG_CASE
   return hipErrorInvalidValue;
 }

@@ -13,5 +13,7 @@ hipError_t launch_t2(int stages, bool vec16, bool bf16, const KArgs& a, hipStrea
 hipError_t launch_t3(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t4(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t5(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t6(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t7(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 
 }  // namespace tcg

@@ -15,16 +15,19 @@ namespace tcg {
 struct TileDesc {
   int id;
   int bm, bn, bk;
-  int wm, wn;  // wave grid
+  int wm, wn;      // wave grid
+  int max_stages;  // deepest LDS ring the kernel is built for
 };
 
 // id 0 is "planner's choice" in the ABI; real ids start at 1.
 constexpr TileDesc kTiles[] = {
-    {1, 256, 256, 64, 2, 2},  // wave 128 x 128: large MFMA-bound products
-    {2, 128, 128, 64, 2, 2},  // wave 64 x 64: mid sizes / more workgroups
-    {3, 64, 64, 64, 2, 2},    // wave 32 x 32: small and ragged products
-    {4, 256, 96, 32, 4, 1},   // wave 64 x 96: short-K, N a multiple of 96
-    {5, 128, 288, 32, 4, 1},  // wave 32 x 288: short-K, N = 288 in one tile
+    {1, 256, 256, 64, 2, 2, 2},  // wave 128 x 128: large MFMA-bound products
+    {2, 128, 128, 64, 2, 2, 2},  // wave 64 x 64: mid sizes / more workgroups
+    {3, 64, 64, 64, 2, 2, 2},    // wave 32 x 32: small and ragged products
+    {4, 256, 96, 32, 4, 1, 2},   // wave 64 x 96: short-K, N a multiple of 96
+    {5, 128, 288, 32, 4, 1, 2},  // wave 32 x 288: short-K, N = 288 in one tile
+    {6, 256, 256, 32, 2, 2, 4},  // wave 128 x 128, half-depth slots: up to 4 in flight
+    {7, 128, 128, 32, 2, 2, 4},  // wave 64 x 64, half-depth slots: up to 4 in flight
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -35,6 +38,7 @@ template <int ID>
 struct Tile {
   static constexpr TileDesc d = kTiles[ID - 1];
   static constexpr int BM = d.bm, BN = d.bn, BK = d.bk, WM = d.wm, WN = d.wn;
+  static constexpr int MAX_STAGES = d.max_stages;
   static constexpr int NW = WM * WN;            // waves per workgroup
   static constexpr int NT = NW * 64;            // lanes per workgroup
   static constexpr int WTM = BM / WM;           // wave tile rows

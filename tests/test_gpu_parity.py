@@ -90,8 +90,32 @@ def test_one_stage_equals_two_stages_bitwise(tcg, name):
     A, B = gw.make_inputs(w)
     C2, _, p2 = run(tcg, A, B, w)
     C1, _, p1 = run(tcg, A, B, w, flags=tcg.FLAG_FORCE_STAGES_1, tile=p2.info().tile_id)
-    assert p2.info().stages == 2 and p1.info().stages == 1
+    assert p2.info().stages >= 2 and p1.info().stages == 1
     assert np.array_equal(as_bits(C1), as_bits(C2))
+
+
+@pytest.mark.parametrize("tile", [6, 7])
+def test_ring_depths_give_the_same_bits(tcg, tile):
+    """Rings of 4, 3 and 2 slots, one stage and no staging: one MFMA
+    sequence, so the same bits (odd and even trip counts, ragged edges)."""
+    for K in (1000, 992, 96):
+        w = gw.custom(520, 300, K, BF16, BF16, EPI_RELU, gw.NORMAL, seed=K)
+        A, B = gw.make_inputs(w)
+        desc = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, tile=tile)
+        ref = None
+        slot = tcg.gemm_plan_for_caps(desc, tcg.make_caps()).info().lds_bytes // 4
+        for lds, flags, want in ((163840, 0, 4), (slot * 7 // 2, 0, 3),
+                                 (163840, tcg.FLAG_FORCE_STAGES_2, 2),
+                                 (163840, tcg.FLAG_FORCE_STAGES_1, 1), (163840, tcg.FLAG_UNSTAGED, 0)):
+            d = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, flags, tile=tile)
+            p = tcg.gemm_plan_for_caps(d, tcg.make_caps(lds_bytes=lds))
+            assert p.info().stages == want
+            bits = as_bits(run(tcg, A, B, w, plan=p)[0])
+            if ref is None:
+                ref = bits
+                check_against_oracle(w, A, B, run(tcg, A, B, w, plan=p)[0])
+            assert np.array_equal(bits, ref), (K, want)
+        del desc
 
 
 def test_repeat_runs_identical(tcg):
@@ -123,7 +147,7 @@ def test_batch_strides(tcg):
     check_against_oracle(w, A, B, C)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7])
 def test_every_tile_gives_the_exact_integer_result(tcg, tile):
     """Every tile configuration computes the same result (page "gizml:tile",
     tune: every configuration must compute the same result)."""
