@@ -142,8 +142,21 @@ def test_degenerate_sizes_plan():
 def test_every_tile_id_plans():
     for t in range(1, tcg.gemm_tile_count() + 1):
         i = plan(1000, 1000, 1000, tile=t).info()
-        assert i.tile_id == t and i.stages == 2
+        assert i.tile_id == t and i.stages >= 2
         assert i.lds_bytes <= 163840
+
+
+def test_deep_ring_follows_lds_budget():
+    """Half-depth tiles keep more chunks in flight where they fit (page
+    "gizml:tile", Program.stages): 4 slots, then 3, capped at 2 on request."""
+    slot = 2 * (256 * 32 + 32 * 256)
+    assert plan(4096, 4096, 4096, tile=6).info().stages == 4
+    assert plan(4096, 4096, 4096, tile=6, caps=tcg.make_caps(lds_bytes=3 * slot)).info().stages == 3
+    assert plan(4096, 4096, 4096, tile=6, caps=tcg.make_caps(lds_bytes=2 * slot)).info().stages == 2
+    assert plan(4096, 4096, 4096, tile=6, caps=tcg.make_caps(lds_bytes=2 * slot - 1)).info().stages == 1
+    assert plan(4096, 4096, 4096, tile=6, flags=tcg.FLAG_FORCE_STAGES_2).info().stages == 2
+    assert plan(4096, 4096, 4096, tile=6, flags=tcg.FLAG_FORCE_STAGES_1).info().stages == 1
+    assert plan(4096, 4096, 4096, tile=6, caps=tcg.make_caps(async_copy=0)).info().stages == 1
 
 
 def test_null_plan_is_rejected():
