@@ -56,16 +56,18 @@ constexpr int kOutF32 = 0, kOutF16 = 4, kOutBF16 = 5;
 // ---------------------------------------------------------------------------
 // LDS layout: row-major slot, 16-byte chunks, chunk index XOR-swizzled by a
 // function of the row.  The XOR value stays below the row's power-of-two
-// chunk group, so the map is a bijection inside every row.
+// chunk group, so the map is a bijection inside every row.  The functions
+// were chosen by measuring fragment-read throughput on gfx950 (whose LDS
+// serves 256-byte lines): for A's 16-byte row reads, rows 2p and 2p+1 share a
+// line, so the XOR follows r/2; for B's transposing 8-byte reads, the four
+// rows a 16-lane group reads are spread by 2(r mod 4) chunks.
 template <int CPR>
 __device__ __forceinline__ int swz_a(int r) {
-  return r & swizzle_mask(CPR);
+  return (r >> 1) & swizzle_mask(CPR);
 }
 template <int CPR>
 __device__ __forceinline__ int swz_b(int r) {
-  // rows 4q .. 4q+3 are XORed with 0, 6, 10, 12 (reduced to the row's mask)
-  const int t = (0xCA60 >> (4 * (r & 3))) & 15;
-  return t & swizzle_mask(CPR);
+  return (2 * (r & 3)) & swizzle_mask(CPR);
 }
 
 // ---------------------------------------------------------------------------
@@ -77,12 +79,57 @@ constexpr int waitcnt_vm_lgkm0() {
   return (N & 15) | ((N >> 4) << 14) | (7 << 4);
 }
 
+// Scheduling of one k-step: the fragment reads of the next k-step (NR LDS
+// reads) are issued two at a time between the first MFMAs of this one, so
+// they have almost the whole k-step to return; the other MFMAs follow.
+template <int NR, int NM>
+__device__ __forceinline__ void interleave_reads_into_mfmas() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  constexpr int pairs = (NR + 1) / 2 < NM ? (NR + 1) / 2 : NM;
+#pragma unroll
+  for (int i = 0; i < pairs; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+  }
+  if (NM > pairs) __builtin_amdgcn_sched_group_barrier(kMfma, NM - pairs, 0);
+}
+
 // A workgroup barrier.  The waits it needs are issued explicitly before it
 // (the waitcnt above); the memory clobber keeps the compiler from moving
 // LDS accesses across it.
 __device__ __forceinline__ void workgroup_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
+
+// ---------------------------------------------------------------------------
+// Buffer resource for raw (unstructured) loads: base address, size in bytes.
+// Offsets at or past the size read 0 (the zero-fill of masked lanes).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+  const uint64_t b = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((b >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(n);
+  r[3] = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+  return r;
+}
+
+// One 16-byte-per-lane copy from a buffer straight into LDS: lane l's 16
+// bytes land at lds_base + 16 l.  Issued as inline assembly so that the
+// compiler's wait insertion does not track it (it cannot tell the ring's
+// slots apart and would drain every copy in flight before some LDS reads);
+// the kernel issues the waits these copies need itself (vmcnt before each
+// barrier).  The copies are the only vector-memory loads of the staged loop.
+__device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t lds_base, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -193,16 +240,16 @@ __device__ __forceinline__ void store_direct(const KArgs& a, const f32x16 (&acc)
 // columns, already rounded) into its own LDS region, then reads the band
 // back row by row and stores 16 bytes per lane, so each store instruction
 // writes whole row segments.
-template <class T>
+template <class T, int OUT>
 __device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (&acc)[T::FM][T::FN], int64_t b,
-                                                  int64_t m0, int64_t n0, int lane, int w, char* smem) {
+                                                  int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {
   constexpr int EPW = T::EPW, EPJ = EPW / 32;
   const int64_t M = a.M, N = a.N;
-  const int osz = a.out_dtype == kOutF32 ? 4 : 2;
-  const int pitch = EPW * osz + 16;  // bytes per band row (padded against bank conflicts)
-  lds_char* band = (lds_char*)smem + w * T::EPI_WAVE_BYTES;
-  const int cpr = EPW * osz / 16;  // 16-byte chunks per band row
-  const int per_elem = 16 / osz;   // elements per chunk
+  constexpr int osz = OUT == kOutF32 ? 4 : 2;
+  constexpr int pitch = EPW * osz + 16;  // bytes per band row (padded against bank conflicts)
+  lds_char* band = smem + w * T::EPI_WAVE_BYTES;
+  constexpr int cpr = EPW * osz / 16;  // 16-byte chunks per band row
+  constexpr int per_elem = 16 / osz;   // elements per chunk
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
 #pragma unroll
@@ -220,8 +267,8 @@ __device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (
           if (osz == 4) {
             *(__attribute__((address_space(3))) f32x4*)(band + row * pitch + col * 4) = f32x4{y[0], y[1], y[2], y[3]};
           } else {
-            const uint32_t lo = pack2(to_out16(y[0], a.out_dtype), to_out16(y[1], a.out_dtype));
-            const uint32_t hi = pack2(to_out16(y[2], a.out_dtype), to_out16(y[3], a.out_dtype));
+            const uint32_t lo = pack2(to_out16(y[0], OUT), to_out16(y[1], OUT));
+            const uint32_t hi = pack2(to_out16(y[2], OUT), to_out16(y[3], OUT));
             *(__attribute__((address_space(3))) u32x2*)(band + row * pitch + col * 2) = u32x2{lo, hi};
           }
         }
@@ -229,7 +276,8 @@ __device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (
       // Same-wave LDS accesses complete in order: the band is readable now.
       const int64_t mb = m0 + 32 * i;
       const int64_t nb = n0 + EPW * jb;
-      const int chunks = 32 * cpr;
+      constexpr int chunks = 32 * cpr;
+#pragma unroll
       for (int idx = lane; idx < chunks; idx += 64) {
         const int r = idx / cpr;
         const int ch = idx - r * cpr;
@@ -272,8 +320,8 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
   const int64_t M = a.M, N = a.N, K = a.K;
   const int64_t row0 = tp.tm * BM;
   const int64_t col0 = tp.tn * BN;
-  const uint16_t* __restrict__ Ab = a.A + tp.b * a.stride_a;
-  const uint16_t* __restrict__ Bb = a.B + tp.b * a.stride_b;
+  const uint16_t* Ab = a.A + tp.b * a.stride_a;
+  const uint16_t* Bb = a.B + tp.b * a.stride_b;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -284,7 +332,7 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;  // Program.zeros
 
   const int trips = a.trips;
-  char* smem_epi = nullptr;
+  lds_char* smem_epi = nullptr;
   (void)smem_epi;
 
   if constexpr (STAGES == 0) {
@@ -341,7 +389,7 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     __shared__ __attribute__((aligned(1024))) char slot1[STAGES >= 2 ? T::SLOT : 16];
     __shared__ __attribute__((aligned(1024))) char slot2[STAGES >= 3 ? T::SLOT : 16];
     __shared__ __attribute__((aligned(1024))) char slot3[STAGES >= 4 ? T::SLOT : 16];
-    smem_epi = slot0;
+    smem_epi = (lds_char*)slot0;
 
     // Copy plan.  Lane position P = i*NT + tid of a slot's chunk array holds
     // the logical chunk (r, c) of the tile with c = (P mod CPR) ^ swz(r): the
@@ -365,11 +413,19 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     const int b_r0 = tid / CPR_B;
     const int b_c80 = 8 * ((tid % CPR_B) ^ swz_b<CPR_B>(b_r0));
     const uint32_t b_off0 = (uint32_t)(b_r0 * N + b_c80) * 2u;
-    auto copy = [&](int t, char* slot) __attribute__((always_inline)) {
+    auto copy = [&](int t, lds_char* slot) __attribute__((always_inline)) {
       const int64_t k0 = (int64_t)t * BK;
       const bool ktail = k0 + BK > K;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + row0 * K + k0, ((M - row0) * K - k0) * 2);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + k0 * N + col0, ((K - k0) * N - col0) * 2);
+      const int64_t a_bytes = ((M - row0) * K - k0) * 2, b_bytes = ((K - k0) * N - col0) * 2;
+      [[maybe_unused]] i32x4 wa, wb;
+      [[maybe_unused]] __amdgpu_buffer_rsrc_t ra, rb;
+      if constexpr (VEC16) {
+        wa = make_rsrc_words(Ab + row0 * K + k0, a_bytes);
+        wb = make_rsrc_words(Bb + k0 * N + col0, b_bytes);
+      } else {
+        ra = make_rsrc(Ab + row0 * K + k0, a_bytes);
+        rb = make_rsrc(Bb + k0 * N + col0, b_bytes);
+      }
 #pragma unroll
       for (int i = 0; i < T::IA; ++i) {
         if (T::CH_A % NT == 0 || (i * NW + w) * 64 < T::CH_A) {  // whole waves only
@@ -384,10 +440,10 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
             c8 = 8 * ((P % CPR_A) ^ swz_a<CPR_A>(r));
             off = (uint32_t)(r * K + c8) * 2u;
           }
-          char* dst = slot + (i * NW + w) * 1024;
+          lds_char* dst = slot + (i * NW + w) * 1024;
           if constexpr (VEC16) {
             const uint32_t o = (ktail && k0 + c8 >= K) ? kOOB : off;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)dst, 16, o, 0, 0, 0);
+            copy16_to_lds(wa, __builtin_amdgcn_readfirstlane(lds_addr(dst)), o);
           } else {
             uint32_t e[8];
 #pragma unroll
@@ -395,12 +451,12 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
               const bool ok = k0 + c8 + q < K;
               e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, ok ? off + 2u * q : kOOB, 0, 0);
             }
-            *(lds_u32x4*)((lds_char*)dst + lane * 16) =
+            *(lds_u32x4*)(dst + lane * 16) =
                 u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
           }
         }
       }
-      char* slotb = slot + T::A_BYTES;
+      lds_char* slotb = slot + T::A_BYTES;
 #pragma unroll
       for (int i = 0; i < T::IB; ++i) {
         if (T::CH_B % NT == 0 || (i * NW + w) * 64 < T::CH_B) {
@@ -415,10 +471,10 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
             c8 = 8 * ((P % CPR_B) ^ swz_b<CPR_B>(r));
             off = (uint32_t)(r * N + c8) * 2u;
           }
-          char* dst = slotb + (i * NW + w) * 1024;
+          lds_char* dst = slotb + (i * NW + w) * 1024;
           if constexpr (VEC16) {
             const uint32_t o = (b_ntail && col0 + c8 >= N) ? kOOB : off;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)dst, 16, o, 0, 0, 0);
+            copy16_to_lds(wb, __builtin_amdgcn_readfirstlane(lds_addr(dst)), o);
           } else {
             uint32_t e[8];
 #pragma unroll
@@ -465,9 +521,9 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     struct Frags {
       u32x4 a[FM], b[FN];
     };
-    auto load = [&](const char* slot, int s, Frags& f) __attribute__((always_inline)) {
-      const lds_char* sa = (const lds_char*)slot;
-      const lds_char* sb = (const lds_char*)slot + T::A_BYTES;
+    auto load = [&](const lds_char* slot, int s, Frags& f) __attribute__((always_inline)) {
+      const lds_char* sa = slot;
+      const lds_char* sb = slot + T::A_BYTES;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
         f.a[i] = *(const lds_u32x4*)(sa + a_base[s] + i * (32 * BK * 2));
@@ -498,49 +554,43 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     Frags f0, f1;
     if constexpr (STAGES >= 2) {
       // A ring of S slots.  Trip t reads slot t mod S while chunks t+1 ..
-      // t+S-1 are in flight into the other slots; at its start it issues the
-      // copy of chunk t+S-1 into slot (t-1) mod S, the slot trip t-1 read.
-      // With S = 2 this is the two-stage pipeline of the page "Module
-      // Tolk.Stage"; more stages hide longer memory latency at the cost of
-      // LDS (page "gizml:tile", Program.stages).
+      // t+S-1 are in flight into the other slots.  With S = 2 this is the
+      // two-stage pipeline of the page "Module Tolk.Stage"; more stages hide
+      // longer memory latency at the cost of LDS (page "gizml:tile",
+      // Program.stages).
       //
       // The one barrier of a trip comes after the last k-step's fragments
       // are in registers and this wave's copy of chunk t+1 has landed: it
-      // retires every read of slot t mod S before trip t+1 overwrites it
-      // (with chunk t+S), and publishes chunk t+1 before it is read.  The
-      // last k-step's MFMAs then run while the first fragments of chunk t+1
-      // load.  Vector-memory loads complete in order, so "chunk t+1 has
-      // landed" is a wait until at most the copies of the newer chunks
-      // (t+2 .. t+S-1, NDMA instructions each) are outstanding.
+      // retires every read of slot t mod S and publishes chunk t+1.  Right
+      // after it the slot just retired is refilled with chunk t+S, so every
+      // copy has S-1 whole trips to land; then the first fragments of chunk
+      // t+1 load while the last k-step's MFMAs run.  Vector-memory loads
+      // complete in order, so "chunk t+1 has landed" is a wait until at most
+      // the copies of the newer chunks (NDMA instructions each) are
+      // outstanding.
       constexpr int S = STAGES;
       static_assert(S == 2 || (T::CH_A % NT == 0 && T::CH_B % NT == 0),
                     "rings deeper than two need whole copy rounds per wave");
       constexpr int NDMA = T::IA + T::IB;  // copy instructions per wave per chunk
-      char* const ring[4] = {slot0, slot1, slot2, slot3};
+      lds_char* const ring[4] = {(lds_char*)slot0, (lds_char*)slot1, (lds_char*)slot2, (lds_char*)slot3};
       auto wait_newer_and_barrier = [&](int newer) __attribute__((always_inline)) {
         // newer: copies of chunks after the awaited one still allowed in flight
-        if constexpr (S >= 4) {
-          if (newer >= 2) { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<2 * NDMA>()); }
-          else if (newer == 1) { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NDMA>()); }
-          else { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>()); }
-        } else if constexpr (S == 3) {
-          if (newer >= 1) { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NDMA>()); }
-          else { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>()); }
+        if (S >= 4 && newer >= 3) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<(S >= 4 ? 3 : 0) * NDMA>());
+        } else if (S >= 3 && newer >= 2) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<(S >= 3 ? 2 : 0) * NDMA>());
+        } else if (newer >= 1) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NDMA>());
         } else {
-          (void)newer;
           __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
         }
         workgroup_barrier();
       };
+      auto newest_issued = [&](int t) { return (t + S - 1 < trips ? t + S - 1 : trips - 1); };
       auto trip = [&](int t, auto J) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
-        char* cur = ring[j];
-        char* cp = ring[(j + S - 1) % S];
-        char* nxt = ring[(j + 1) % S];
-        // The copy is issued first and kept there: the scheduler may not
-        // sink it towards the barrier, where it would no longer overlap.
-        if (t + S - 1 < trips) copy(t + S - 1, cp);
-        __builtin_amdgcn_sched_barrier(0);
+        lds_char* cur = ring[j];
+        lds_char* nxt = ring[(j + 1) % S];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           Frags& now = (s & 1) ? f1 : f0;
@@ -548,22 +598,25 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
           if (s + 1 < KS) {
             load(cur, s + 1, next);
             mma(now);
+            interleave_reads_into_mfmas<FM + 2 * FN, FM * FN>();
           } else {
-            const int issued_after = (t + S - 1 < trips ? t + S - 1 : trips - 1) - (t + 1);
-            wait_newer_and_barrier(issued_after > 0 ? issued_after : 0);
+            const int newer = newest_issued(t) - (t + 1);
+            wait_newer_and_barrier(newer > 0 ? newer : 0);
+            if (t + S < trips) copy(t + S, cur);
             if (t + 1 < trips) load(nxt, 0, next);
             mma(now);
+            interleave_reads_into_mfmas<FM + 2 * FN, FM * FN>();
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       };
       if (trips > 0) {
 #pragma unroll
-        for (int c = 0; c < S - 1; ++c)
+        for (int c = 0; c < S; ++c)
           if (c < trips) copy(c, ring[c]);
-        const int issued_after = (S - 2 < trips - 1 ? S - 2 : trips - 1);
-        wait_newer_and_barrier(issued_after > 0 ? issued_after : 0);
-        load(slot0, 0, f0);
+        const int newer = (S - 1 < trips - 1 ? S - 1 : trips - 1);
+        wait_newer_and_barrier(newer);
+        load(ring[0], 0, f0);
       }
       // Unrolled by S so that each copy and each read names one slot; the
       // last trips are peeled so the loop body has no branch around a whole
@@ -589,14 +642,14 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
       }
     } else {
       for (int t = 0; t < trips; ++t) {
-        copy(t, slot0);
+        copy(t, (lds_char*)slot0);
         wait_all_and_barrier();  // publishes the tile
-        load(slot0, 0, f0);
+        load((lds_char*)slot0, 0, f0);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           Frags& now = (s & 1) ? f1 : f0;
           Frags& next = (s & 1) ? f0 : f1;
-          if (s + 1 < KS) load(slot0, s + 1, next);
+          if (s + 1 < KS) load((lds_char*)slot0, s + 1, next);
           mma(now);
         }
         wait_all_and_barrier();  // retires the reads before the next copy
@@ -610,7 +663,12 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
   if constexpr (STAGES == 0) {
     store_direct<T>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane);
   } else {
-    store_through_lds<T>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane, w, smem_epi);
+    if (a.out_dtype == kOutF32)
+      store_through_lds<T, kOutF32>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane, w, smem_epi);
+    else if (a.out_dtype == kOutBF16)
+      store_through_lds<T, kOutBF16>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane, w, smem_epi);
+    else
+      store_through_lds<T, kOutF16>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane, w, smem_epi);
   }
 }
 
