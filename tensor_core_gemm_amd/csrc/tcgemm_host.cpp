@@ -98,14 +98,12 @@ int tile_occupancy(int id) {
 }
 
 // Choose a tile for the problem: short-K products whose N is a multiple of
-// 288 or 96 take the wide-N tiles (one read of A, few trips); the rest take
-// the general tile with the lowest estimated time (whole rounds of
-// workgroups over the CUs times the per-tile MFMA work).
+// 96 take the 256 x 96 tile (few trips, many workgroups to stream A and C;
+// measured faster than one 128 x 288 tile per row block); the rest take the
+// general tile with the lowest estimated time (whole rounds of workgroups
+// over the CUs times the per-tile MFMA work).
 int choose_tile(const gemm_desc& d, const gemm_device_caps& caps) {
-  if (d.K <= 128 && d.N > 0) {
-    if (d.N % 288 == 0) return 5;
-    if (d.N % 96 == 0) return 4;
-  }
+  if (d.K <= 128 && d.N > 0 && d.N % 96 == 0) return 4;
   int best = 1;
   double best_t = 1e300;
   for (int id = 1; id <= 3; ++id) {

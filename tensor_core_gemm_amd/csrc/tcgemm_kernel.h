@@ -403,7 +403,8 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     // read 0 by themselves; the K tail of A (last trip) and the N tail of B
     // (last tile column) are masked with an out-of-range offset.
     const bool b_ntail = col0 + BN > N;
-    constexpr bool SIMPLE_A = (NT % CPR_A == 0) && ((NT / CPR_A) % (swizzle_mask(CPR_A) + 1) == 0) &&
+    // (swz_a repeats every 2 (mask + 1) rows, swz_b every 4 rows)
+    constexpr bool SIMPLE_A = (NT % CPR_A == 0) && ((NT / CPR_A) % (2 * (swizzle_mask(CPR_A) + 1)) == 0) &&
                               (T::CH_A % NT == 0);
     constexpr bool SIMPLE_B = (NT % CPR_B == 0) && ((NT / CPR_B) % 4 == 0) && (T::CH_B % NT == 0);
     // Per-lane chunk of round 0 (rounds add NT / CPR rows).
@@ -413,21 +414,64 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     const int b_r0 = tid / CPR_B;
     const int b_c80 = 8 * ((tid % CPR_B) ^ swz_b<CPR_B>(b_r0));
     const uint32_t b_off0 = (uint32_t)(b_r0 * N + b_c80) * 2u;
-    auto copy = [&](int t, lds_char* slot) __attribute__((always_inline)) {
+    // Copy chunk (trip) t with element loads (rows not 16-byte aligned).
+    auto copy_elements = [&](int t, lds_char* slot) __attribute__((always_inline)) {
       const int64_t k0 = (int64_t)t * BK;
-      const bool ktail = k0 + BK > K;
-      const int64_t a_bytes = ((M - row0) * K - k0) * 2, b_bytes = ((K - k0) * N - col0) * 2;
-      [[maybe_unused]] i32x4 wa, wb;
-      [[maybe_unused]] __amdgpu_buffer_rsrc_t ra, rb;
-      if constexpr (VEC16) {
-        wa = make_rsrc_words(Ab + row0 * K + k0, a_bytes);
-        wb = make_rsrc_words(Bb + k0 * N + col0, b_bytes);
-      } else {
-        ra = make_rsrc(Ab + row0 * K + k0, a_bytes);
-        rb = make_rsrc(Bb + k0 * N + col0, b_bytes);
-      }
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + row0 * K + k0, ((M - row0) * K - k0) * 2);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + k0 * N + col0, ((K - k0) * N - col0) * 2);
 #pragma unroll
       for (int i = 0; i < T::IA; ++i) {
+        if (T::CH_A % NT == 0 || (i * NW + w) * 64 < T::CH_A) {
+          const int P = i * NT + tid;
+          const int r = P / CPR_A;
+          const int c8 = 8 * ((P % CPR_A) ^ swz_a<CPR_A>(r));
+          const uint32_t off = (uint32_t)(r * K + c8) * 2u;
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const bool ok = k0 + c8 + q < K;
+            e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, ok ? off + 2u * q : kOOB, 0, 0);
+          }
+          *(lds_u32x4*)(slot + (i * NW + w) * 1024 + lane * 16) =
+              u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < T::IB; ++i) {
+        if (T::CH_B % NT == 0 || (i * NW + w) * 64 < T::CH_B) {
+          const int P = i * NT + tid;
+          const int r = P / CPR_B;
+          const int c8 = 8 * ((P % CPR_B) ^ swz_b<CPR_B>(r));
+          const uint32_t off = (uint32_t)(r * N + c8) * 2u;
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const bool ok = col0 + c8 + q < N;
+            e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, ok ? off + 2u * q : kOOB, 0, 0);
+          }
+          *(lds_u32x4*)(slot + T::A_BYTES + (i * NW + w) * 1024 + lane * 16) =
+              u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+        }
+      }
+    };
+    // Per-trip copy state and one copy instruction (round q: A rounds
+    // first, then B rounds) of the 16-byte path.
+    struct CopyCtx {
+      int64_t k0;
+      bool ktail;
+      i32x4 wa, wb;
+    };
+    auto copy_ctx = [&](int t) __attribute__((always_inline)) {
+      CopyCtx c;
+      c.k0 = (int64_t)t * BK;
+      c.ktail = c.k0 + BK > K;
+      c.wa = make_rsrc_words(Ab + row0 * K + c.k0, ((M - row0) * K - c.k0) * 2);
+      c.wb = make_rsrc_words(Bb + c.k0 * N + col0, ((K - c.k0) * N - col0) * 2);
+      return c;
+    };
+    auto copy_part = [&](const CopyCtx& c, lds_char* slot, int q) __attribute__((always_inline)) {
+      if (q < T::IA) {
+        const int i = q;
         if (T::CH_A % NT == 0 || (i * NW + w) * 64 < T::CH_A) {  // whole waves only
           int c8;
           uint32_t off;
@@ -441,24 +485,11 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
             off = (uint32_t)(r * K + c8) * 2u;
           }
           lds_char* dst = slot + (i * NW + w) * 1024;
-          if constexpr (VEC16) {
-            const uint32_t o = (ktail && k0 + c8 >= K) ? kOOB : off;
-            copy16_to_lds(wa, __builtin_amdgcn_readfirstlane(lds_addr(dst)), o);
-          } else {
-            uint32_t e[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const bool ok = k0 + c8 + q < K;
-              e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, ok ? off + 2u * q : kOOB, 0, 0);
-            }
-            *(lds_u32x4*)(dst + lane * 16) =
-                u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-          }
+          const uint32_t o = (c.ktail && c.k0 + c8 >= K) ? kOOB : off;
+          copy16_to_lds(c.wa, __builtin_amdgcn_readfirstlane(lds_addr(dst)), o);
         }
-      }
-      lds_char* slotb = slot + T::A_BYTES;
-#pragma unroll
-      for (int i = 0; i < T::IB; ++i) {
+      } else {
+        const int i = q - T::IA;
         if (T::CH_B % NT == 0 || (i * NW + w) * 64 < T::CH_B) {
           int c8;
           uint32_t off;
@@ -471,21 +502,20 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
             c8 = 8 * ((P % CPR_B) ^ swz_b<CPR_B>(r));
             off = (uint32_t)(r * N + c8) * 2u;
           }
-          lds_char* dst = slotb + (i * NW + w) * 1024;
-          if constexpr (VEC16) {
-            const uint32_t o = (b_ntail && col0 + c8 >= N) ? kOOB : off;
-            copy16_to_lds(wb, __builtin_amdgcn_readfirstlane(lds_addr(dst)), o);
-          } else {
-            uint32_t e[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const bool ok = col0 + c8 + q < N;
-              e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, ok ? off + 2u * q : kOOB, 0, 0);
-            }
-            *(lds_u32x4*)((lds_char*)dst + lane * 16) =
-                u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-          }
+          lds_char* dst = slot + T::A_BYTES + (i * NW + w) * 1024;
+          const uint32_t o = (b_ntail && col0 + c8 >= N) ? kOOB : off;
+          copy16_to_lds(c.wb, __builtin_amdgcn_readfirstlane(lds_addr(dst)), o);
         }
+      }
+    };
+    // Copy chunk (trip) t into a slot.
+    auto copy = [&](int t, lds_char* slot) __attribute__((always_inline)) {
+      if constexpr (VEC16) {
+        const CopyCtx c = copy_ctx(t);
+#pragma unroll
+        for (int q = 0; q < T::IA + T::IB; ++q) copy_part(c, slot, q);
+      } else {
+        copy_elements(t, slot);
       }
     };
 
@@ -539,6 +569,24 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
         }
         f.b[j] = u32x4{v[0], v[1], v[2], v[3]};
       }
+    };
+    // Single fragment reads (read r of a k-step: A blocks first, then the
+    // two halves of each B block) and single MFMAs, for hand-interleaving.
+    constexpr int NREADS = FM + 2 * FN;
+    auto load_one = [&](const lds_char* slot, int s, Frags& f, int r) __attribute__((always_inline)) {
+      if (r < FM) {
+        f.a[r] = *(const lds_u32x4*)(slot + a_base[s] + r * (32 * BK * 2));
+      } else {
+        const int j = (r - FM) >> 1, h = (r - FM) & 1;
+        const lds_char* p = slot + T::A_BYTES + b_base[j] + (16 * s + 4 * h) * (BN * 2);
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        f.b[j][2 * h] = pack2((uint16_t)x[0], (uint16_t)x[1]);
+        f.b[j][2 * h + 1] = pack2((uint16_t)x[2], (uint16_t)x[3]);
+      }
+    };
+    auto mma_one = [&](const Frags& f, int m) __attribute__((always_inline)) {
+      const int i = m / FN, j = m % FN;
+      acc[i][j] = mfma<BF16IN>(f.b[j], f.a[i], acc[i][j]);
     };
     auto mma = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -610,6 +658,41 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       };
+      // The same trip where chunk t+S exists and chunk t+1 follows (every
+      // trip but the last S): the last k-step is interleaved by hand, one
+      // read of the next chunk's first fragments and one copy instruction
+      // between consecutive MFMAs, so the MFMA pipe keeps running while the
+      // refill and the reads issue.
+      auto trip_fast = [&](int t, auto J) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value;
+        lds_char* cur = ring[j];
+        lds_char* nxt = ring[(j + 1) % S];
+#pragma unroll
+        for (int s = 0; s + 1 < KS; ++s) {
+          Frags& now = (s & 1) ? f1 : f0;
+          Frags& next = (s & 1) ? f0 : f1;
+          load(cur, s + 1, next);
+          mma(now);
+          interleave_reads_into_mfmas<NREADS, FM * FN>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        Frags& now = ((KS - 1) & 1) ? f1 : f0;
+        Frags& next = ((KS - 1) & 1) ? f0 : f1;
+        const int newer = newest_issued(t) - (t + 1);
+        wait_newer_and_barrier(newer > 0 ? newer : 0);
+        const CopyCtx c = copy_ctx(t + S);
+        constexpr int NM = FM * FN, ND = T::IA + T::IB;
+        constexpr int RPM = (NREADS + NM - 1) / NM, DPM = (ND + NM - 1) / NM;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+#pragma unroll
+          for (int r = m * RPM; r < (m + 1) * RPM && r < NREADS; ++r) load_one(nxt, 0, next, r);
+#pragma unroll
+          for (int q = m * DPM; q < (m + 1) * DPM && q < ND; ++q) copy_part(c, cur, q);
+          mma_one(now, m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
       if (trips > 0) {
 #pragma unroll
         for (int c = 0; c < S; ++c)
@@ -627,6 +710,14 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
       using I2 = std::integral_constant<int, 2>;
       using I3 = std::integral_constant<int, 3>;
       int t = 0;
+      if constexpr (VEC16) {
+        for (; t + 2 * S <= trips; t += S) {
+          trip_fast(t, I0{});
+          trip_fast(t + 1, I1{});
+          if constexpr (S >= 3) trip_fast(t + 2, I2{});
+          if constexpr (S >= 4) trip_fast(t + 3, I3{});
+        }
+      }
       for (; t + S <= trips; t += S) {
         trip(t, I0{});
         trip(t + 1, I1{});

@@ -94,7 +94,7 @@ def test_stage_fallbacks_follow_lds_budget():
 
 def test_short_k_token_projection_takes_wide_tile():
     i = plan(129600, 288, 96, F16, F16, EPI_NONE).info()
-    assert i.bn == 288 and i.tiles_n == 1 and i.trips == 3
+    assert (i.bm, i.bn, i.bk) == (256, 96, 32) and i.tiles_n == 3 and i.trips == 3
 
 
 def test_ragged_and_small_shapes_fill_the_chip():
