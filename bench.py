@@ -36,7 +36,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bf16_4096_relu")
     ap.add_argument("--tile", type=int, default=0, help="force a tile configuration id")
     ap.add_argument("--flags", type=int, default=0, help="plan flags (1: one stage, 2: unstaged)")
@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the GEMM, run a plain device copy of this many MiB three "
                          "times (a known-size reference for the HBM byte counters)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
     return ap.parse_args()
 
@@ -104,18 +104,21 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # One event pair around the K launches on the launch stream: the
+    # average launch duration is the region's device time over K (events
+    # between launches would add their own overhead to every launch).
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record(stream)
+    e_start.record(stream)
     for i in range(K):
         step(i)
-        ev[i + 1].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    durs_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
-    avg_launch_ms = sum(durs_ms) / K
+    avg_launch_ms = e_start.elapsed_time(e_end) / K
     ms_per_step = (t1 - t0) * 1e3 / K
 
     flops = w.flops

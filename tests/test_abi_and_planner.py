@@ -99,9 +99,11 @@ def test_short_k_token_projection_takes_wide_tile():
 
 def test_ragged_and_small_shapes_fill_the_chip():
     i = plan(1000, 1000, 1000, F16, F32).info()
-    assert i.workgroups >= 200
+    assert (i.bm, i.workgroups) == (64, 256)
     i = plan(2048, 2048, 16384, BF16, BF16, EPI_NONE).info()
-    assert i.workgroups >= 256
+    assert (i.bm, i.bn, i.workgroups) == (128, 128, 256)
+    i = plan(256, 256, 256, F16, F32).info()
+    assert i.bm == 64
 
 
 def test_vec16_needs_aligned_rows():

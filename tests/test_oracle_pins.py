@@ -304,6 +304,22 @@ def test_batch_items_follow_their_strides():
         assert np.array_equal(C[b_], _emulate(a, b, EPI_RELU, F32))
 
 
+@pytest.mark.parametrize("in_dtype,out_dtype", [(F16, F32), (BF16, BF16)])
+def test_sampled_brute_force(in_dtype, out_dtype):
+    """The sampled entry point against the Python fp32 emulation directly."""
+    rng = np.random.default_rng(21 + in_dtype)
+    M, N, K = 9, 11, 37
+    a = values_of(in_dtype, bits_of(in_dtype, rng.standard_normal((M, K))))
+    b = values_of(in_dtype, bits_of(in_dtype, rng.standard_normal((K, N))))
+    ii, jj = rng.integers(0, M, 40), rng.integers(0, N, 40)
+    for epi in (EPI_NONE, EPI_RELU):
+        want = _emulate(a, b, epi, out_dtype)[ii, jj]
+        got, _ = oracle.gemm_sampled(bits_of(in_dtype, a), bits_of(in_dtype, b), M, N, K, in_dtype,
+                                     out_dtype, epi, np.zeros(40), ii, jj)
+        kind = np.uint32 if out_dtype == F32 else np.uint16
+        assert np.array_equal(got.view(kind), want.view(kind))
+
+
 def test_sampled_equals_full():
     rng = np.random.default_rng(13)
     M, N, K = 40, 50, 77
