@@ -58,12 +58,23 @@ constexpr int kOutF32 = 0, kOutF16 = 4, kOutBF16 = 5;
 // function of the row.  The XOR value stays below the row's power-of-two
 // chunk group, so the map is a bijection inside every row.  The functions
 // were chosen by measuring fragment-read throughput on gfx950 (whose LDS
-// serves 256-byte lines): for A's 16-byte row reads, rows 2p and 2p+1 share a
-// line, so the XOR follows r/2; for B's transposing 8-byte reads, the four
-// rows a 16-lane group reads are spread by 2(r mod 4) chunks.
+// serves 256-byte lines): for A's 16-byte row reads, the 16 rows that 16
+// lanes read must land on 16 different 16-byte bank groups; 16 / CPR rows
+// share a line, so the XOR follows r / (16 / CPR) (r/2 for 64-deep slots,
+// r/4 for 32-deep ones).  For B's transposing 8-byte reads, the four rows a
+// 16-lane group reads are spread by 2(r mod 4) chunks.
+template <int CPR>
+constexpr int swz_a_shift() {
+  return CPR >= 16 ? 0 : CPR >= 8 ? 1 : CPR >= 4 ? 2 : CPR >= 2 ? 3 : 4;
+}
+// Rows after which swz_a repeats.
+template <int CPR>
+constexpr int swz_a_period() {
+  return (1 << swz_a_shift<CPR>()) * (swizzle_mask(CPR) + 1);
+}
 template <int CPR>
 __device__ __forceinline__ int swz_a(int r) {
-  return (r >> 1) & swizzle_mask(CPR);
+  return (r >> swz_a_shift<CPR>()) & swizzle_mask(CPR);
 }
 template <int CPR>
 __device__ __forceinline__ int swz_b(int r) {
@@ -402,9 +413,10 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     // last element, so A rows past M and B rows past K are out of range and
     // read 0 by themselves; the K tail of A (last trip) and the N tail of B
     // (last tile column) are masked with an out-of-range offset.
+    static_assert(T::CH_A % 64 == 0 && T::CH_B % 64 == 0, "copy rounds are whole waves");
     const bool b_ntail = col0 + BN > N;
-    // (swz_a repeats every 2 (mask + 1) rows, swz_b every 4 rows)
-    constexpr bool SIMPLE_A = (NT % CPR_A == 0) && ((NT / CPR_A) % (2 * (swizzle_mask(CPR_A) + 1)) == 0) &&
+    // (swz_a repeats every swz_a_period rows, swz_b every 4 rows)
+    constexpr bool SIMPLE_A = (NT % CPR_A == 0) && ((NT / CPR_A) % swz_a_period<CPR_A>() == 0) &&
                               (T::CH_A % NT == 0);
     constexpr bool SIMPLE_B = (NT % CPR_B == 0) && ((NT / CPR_B) % 4 == 0) && (T::CH_B % NT == 0);
     // Per-lane chunk of round 0 (rounds add NT / CPR rows).
@@ -534,6 +546,7 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     // 4q .. 4q+3, and lane x receives column x.  The row is
     // 16s + 8(l/32) + 4h + ((l mod 16) / 4), whose swizzle depends only on
     // l, so the lane's byte offset is b_base[j] + (16s + 4h) * BN * 2.
+    static_assert(32 % swz_a_period<CPR_A>() == 0, "A fragment rows must start on a swizzle period");
     int a_base[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -615,11 +628,14 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
       // t+1 load while the last k-step's MFMAs run.  Vector-memory loads
       // complete in order, so "chunk t+1 has landed" is a wait until at most
       // the copies of the newer chunks (NDMA instructions each) are
-      // outstanding.
+      // outstanding.  Where a copy round is partial (CH not a multiple of
+      // NT) the first waves issue one instruction more per chunk than the
+      // last; NDMA counts only the instructions every wave issues, so a wave
+      // with more waits a little longer than it must, and none too little.
       constexpr int S = STAGES;
       static_assert(S == 2 || (T::CH_A % NT == 0 && T::CH_B % NT == 0),
                     "rings deeper than two need whole copy rounds per wave");
-      constexpr int NDMA = T::IA + T::IB;  // copy instructions per wave per chunk
+      constexpr int NDMA = T::CH_A / NT + T::CH_B / NT;  // copies every wave issues per chunk
       lds_char* const ring[4] = {(lds_char*)slot0, (lds_char*)slot1, (lds_char*)slot2, (lds_char*)slot3};
       auto wait_newer_and_barrier = [&](int newer) __attribute__((always_inline)) {
         // newer: copies of chunks after the awaited one still allowed in flight

@@ -73,6 +73,31 @@ def test_full_size_sampled(tcg, name):
     check_sampled(w, A, B, C)
 
 
+@pytest.mark.parametrize("tile", [4, 5])
+def test_swin_full_size_every_output(tcg, tile):
+    """The Swin projection at full size on both short-K tiles, every output
+    checked: the last tile row is ragged (129600 = 506 x 256 + 64) and the B
+    copies are partial rounds, so the wait for the first chunk must count
+    the copies of the waves that issue fewer."""
+    w = W["swin_proj_fp16"]
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w, tile=tile)
+    assert p.info().tile_id == tile
+    check_against_oracle(w, A, B, C)
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_full_size_runs_are_bitwise_stable(tcg, name):
+    """Three launches of the benchmark's plan give the same bits: a missing
+    wait or barrier shows up as run-to-run differences."""
+    w = W[name]
+    A, B = gw.make_inputs(w)
+    C0, _, p = run(tcg, A, B, w)
+    first = as_bits(C0)
+    for _ in range(2):
+        assert np.array_equal(as_bits(run(tcg, A, B, w, plan=p)[0]), first)
+
+
 @pytest.mark.parametrize("name", list(W))
 def test_staged_equals_unstaged_bitwise(tcg, name):
     w = W[name]
