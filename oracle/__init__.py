@@ -10,8 +10,11 @@ code, header, table or constant.  Inputs cross over as raw 16-bit patterns
 The arithmetic lives in ``oracle.c`` (plain C, built with gcc and OpenMP,
 ``-ffp-contract=off``).  It follows the worked example of the page
 "gizml:tile": a zero accumulator (Program.zeros), a fold over k in ascending
-order (Program.fold), products and sums in F32 (Tile.dot), max(x, 0)
-(Tile.relu, with Tile.maximum's NaN rule), then rounding to the storage type
+order (Program.fold), products and sums in F32 (Tile.dot), an optional
+bias row added in F32 (Tile.add, broadcast over rows), an activation
+(Tile.relu with Tile.maximum's NaN rule, Tile.gelu, Tile.geluErf,
+Tile.sigmoid, Tile.tanh; the transcendental ones from their definitions in
+double precision, rounded once to F32), then rounding to the storage type
 (Tile.to).  Storage codes are the page's constants: F32 = 0, F16 = 4,
 BF16 = 5.
 """
@@ -25,7 +28,7 @@ import threading
 import numpy as np
 
 F32, F16, BF16 = 0, 4, 5
-EPI_NONE, EPI_RELU = 0, 1
+EPI_NONE, EPI_RELU, EPI_GELU, EPI_GELU_ERF, EPI_SIGMOID, EPI_TANH = 0, 1, 2, 3, 4, 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -62,12 +65,12 @@ def _load():
             lib.oracle_encode.restype = None
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = _int
-            lib.oracle_gemm.argtypes = [_i64, _i64, _i64, _int, _int, _int, _i64, _vp, _i64, _vp,
-                                        _i64, _vp, _i64, _vp, _int]
+            lib.oracle_gemm.argtypes = [_i64, _i64, _i64, _int, _int, _int, _vp, _i64, _vp, _i64,
+                                        _vp, _i64, _vp, _i64, _vp, _int]
             lib.oracle_gemm.restype = _int
-            lib.oracle_gemm_sampled.argtypes = [_i64, _i64, _i64, _int, _int, _int, _i64, _vp,
-                                                _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
-                                                _int]
+            lib.oracle_gemm_sampled.argtypes = [_i64, _i64, _i64, _int, _int, _int, _vp, _i64,
+                                                _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
+                                                _vp, _int]
             lib.oracle_gemm_sampled.restype = _int
             lib.oracle_gemm_f64.argtypes = [_i64, _i64, _i64, _int, _i64, _vp, _i64, _vp, _i64,
                                             _vp, _vp, _int]
@@ -115,6 +118,18 @@ def encode(dtype: int, values) -> np.ndarray:
     return out
 
 
+def _bias(bias, N: int):
+    """bias -> (keep-alive array or None, pointer or None)."""
+    if bias is None:
+        return None, None
+    if hasattr(bias, "detach"):
+        bias = bias.detach().cpu().float().numpy()
+    v = np.ascontiguousarray(bias, np.float32).reshape(-1)
+    if v.size != N:
+        raise ValueError("bias must hold N values")
+    return v, _ptr(v)
+
+
 def _check(rc: int):
     if rc != 0:
         raise ValueError({-1: "bad argument", -2: "bad dtype", -3: "out of memory"}.get(rc, rc))
@@ -122,8 +137,9 @@ def _check(rc: int):
 
 def gemm(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, epilogue: int,
          batch: int = 1, stride_a: int | None = None, stride_b: int | None = None,
-         want_y: bool = False, n_threads: int = 0):
-    """C = epilogue(A . B) for [batch][M][K] x [batch][K][N] row-major operands.
+         want_y: bool = False, n_threads: int = 0, bias=None):
+    """C = act(A . B + bias) for [batch][M][K] x [batch][K][N] row-major operands
+    (epilogue: the activation code; bias: N fp32 values or None).
 
     Returns C as float32 (out F32) or uint16 patterns (F16/BF16), shape
     [batch, M, N], and, if ``want_y``, the fp32 value before rounding too.
@@ -135,7 +151,8 @@ def gemm(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, epilogue: 
         raise ValueError("operand arrays smaller than the shape and strides need")
     C = np.zeros((batch, M, N), np.float32 if out_dtype == F32 else np.uint16)
     Y = np.zeros((batch, M, N), np.float32) if want_y else None
-    _check(_load().oracle_gemm(M, N, K, in_dtype, out_dtype, epilogue, batch, _ptr(a), sa,
+    keep, bp = _bias(bias, N)
+    _check(_load().oracle_gemm(M, N, K, in_dtype, out_dtype, epilogue, bp, batch, _ptr(a), sa,
                                _ptr(b), sb, _ptr(C), M * N, _ptr(Y) if Y is not None else None,
                                n_threads))
     return (C, Y) if want_y else C
@@ -143,7 +160,7 @@ def gemm(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, epilogue: 
 
 def gemm_sampled(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, epilogue: int,
                  bi, ii, jj, batch: int = 1, stride_a: int | None = None,
-                 stride_b: int | None = None, n_threads: int = 0):
+                 stride_b: int | None = None, n_threads: int = 0, bias=None):
     """The oracle for the listed elements C[bi[e], ii[e], jj[e]] only.
 
     Returns (values in out_dtype storage, fp32 y before rounding).
@@ -160,7 +177,8 @@ def gemm_sampled(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, ep
         raise ValueError("operand arrays smaller than the shape and strides need")
     out = np.zeros(ii.shape, np.float32 if out_dtype == F32 else np.uint16)
     Y = np.zeros(ii.shape, np.float32)
-    _check(_load().oracle_gemm_sampled(M, N, K, in_dtype, out_dtype, epilogue, batch, _ptr(a),
+    keep, bp = _bias(bias, N)
+    _check(_load().oracle_gemm_sampled(M, N, K, in_dtype, out_dtype, epilogue, bp, batch, _ptr(a),
                                        sa, _ptr(b), sb, ii.size, _ptr(bi), _ptr(ii), _ptr(jj),
                                        _ptr(out), _ptr(Y), n_threads))
     return out, Y

@@ -16,8 +16,20 @@
  *         acc = +0.0f                                   (Program.zeros)
  *         for k = 0, 1, ..., K-1:                        (Program.fold)
  *             acc = fl32(acc + fl32(f32(A[b,i,k]) * f32(B[b,k,j])))   (Tile.dot: F32)
- *         y = relu ? (acc > 0 ? acc : +0.0f) : acc       (Tile.relu; Tile.maximum's NaN rule)
+ *         v = bias ? fl32(acc + bias[j]) : acc          (Tile.add, a [1, N] row broadcast)
+ *         y = act(v)                                    (Tile.relu, gelu, geluErf, sigmoid, tanh)
  *         C[b,i,j] = round_to_nearest_even(y, out_dtype) (Tile.to: "as a store and a load")
+ *
+ * Activations (codes 0 none, 1 relu, 2 gelu, 3 geluErf, 4 sigmoid, 5 tanh)
+ * follow their definitions on the page, evaluated in double precision from
+ * the fp32 value v and rounded once to fp32 (the page asks for results
+ * within a few ulp; this is the correctly rounded value up to double's own
+ * error):
+ *     relu(v)    = v > 0 ? v : +0
+ *     gelu(v)    = v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3)))   (tanh form)
+ *     geluErf(v) = v/2 * (1 + erf(v / sqrt(2)))                          (erf form)
+ *     sigmoid(v) = 1 / (1 + e^-v)
+ *     tanh(v)    = tanh(v)
  *
  * Readings taken where the page is silent (each is also listed with the
  * design notes):
@@ -150,13 +162,32 @@ void oracle_encode(int dtype, const float* src, uint16_t* dst, int64_t n) {
 static int orc_check(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int epilogue,
                      int64_t batch) {
   if (M < 0 || N < 0 || K < 0 || batch < 1) return ORC_EARG;
-  if (epilogue != 0 && epilogue != 1) return ORC_EARG;
+  if (epilogue < 0 || epilogue > 5) return ORC_EARG;
   if (in_dtype != ORC_F16 && in_dtype != ORC_BF16) return ORC_EDTYPE;
   if (out_dtype != ORC_F32 && out_dtype != ORC_F16 && out_dtype != ORC_BF16) return ORC_EDTYPE;
   return ORC_OK;
 }
 
 static float orc_relu(float v) { return (v > 0.0f) ? v : 0.0f; }
+
+static float orc_activate(float v, int act) {
+  const double x = (double)v;
+  const double pi = 3.14159265358979323846;
+  switch (act) {
+    case 0: return v;
+    case 1: return orc_relu(v);
+    case 2: return (float)(0.5 * x * (1.0 + tanh(sqrt(2.0 / pi) * (x + 0.044715 * x * x * x))));
+    case 3: return (float)(0.5 * x * (1.0 + erf(x / sqrt(2.0))));
+    case 4: return (float)(1.0 / (1.0 + exp(-x)));
+    default: return (float)tanh(x);
+  }
+}
+
+/* The epilogue of one output: bias (when given), then the activation. */
+static float orc_epilogue(float acc, const float* bias, int64_t j, int act) {
+  const float v = bias ? acc + bias[j] : acc;
+  return orc_activate(v, act);
+}
 
 static void orc_store(int out_dtype, void* C, int64_t idx, float y) {
   if (out_dtype == ORC_F32)
@@ -186,12 +217,14 @@ int oracle_max_threads(void) {
 /*
  * Full GEMM.  A is [batch][M][K], B is [batch][K][N], C is [batch][M][N],
  * each row-major with contiguous rows; stride_* is the element distance
- * between batch items.  Y, when not NULL, receives the fp32 value y before
- * the output conversion, as a contiguous [batch][M][N] array.
+ * between batch items.  bias, when not NULL, holds N fp32 values added to
+ * every row.  Y, when not NULL, receives the fp32 value y before the output
+ * conversion, as a contiguous [batch][M][N] array.
  */
 int oracle_gemm(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int epilogue,
-                int64_t batch, const uint16_t* A, int64_t stride_a, const uint16_t* B,
-                int64_t stride_b, void* C, int64_t stride_c, float* Y, int threads) {
+                const float* bias, int64_t batch, const uint16_t* A, int64_t stride_a,
+                const uint16_t* B, int64_t stride_b, void* C, int64_t stride_c, float* Y,
+                int threads) {
   int rc = orc_check(M, N, K, in_dtype, out_dtype, epilogue, batch);
   if (rc) return rc;
   if (M == 0 || N == 0) return ORC_OK;
@@ -213,7 +246,7 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, in
         for (int64_t j = 0; j < N; ++j) acc[j] = acc[j] + a * brow[j];
       }
       for (int64_t j = 0; j < N; ++j) {
-        float y = epilogue ? orc_relu(acc[j]) : acc[j];
+        float y = orc_epilogue(acc[j], bias, j, epilogue);
         orc_store(out_dtype, C, b * stride_c + i * N + j, y);
         if (Y) Y[(b * M + i) * N + j] = y;
       }
@@ -232,7 +265,8 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, in
  * and, when Y is not NULL, its fp32 y to Y[e].  Same sum order as above.
  */
 int oracle_gemm_sampled(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
-                        int epilogue, int64_t batch, const uint16_t* A, int64_t stride_a,
+                        int epilogue, const float* bias, int64_t batch, const uint16_t* A,
+                        int64_t stride_a,
                         const uint16_t* B, int64_t stride_b, int64_t count, const int64_t* bi,
                         const int64_t* ii, const int64_t* jj, void* out, float* Y, int threads) {
   int rc = orc_check(M, N, K, in_dtype, out_dtype, epilogue, batch);
@@ -252,7 +286,7 @@ int oracle_gemm_sampled(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
       float bv = (in_dtype == ORC_F16) ? orc_f16_decode(bcol[k * N]) : orc_bf16_decode(bcol[k * N]);
       acc = acc + a * bv;
     }
-    float y = epilogue ? orc_relu(acc) : acc;
+    float y = orc_epilogue(acc, bias, jj[e], epilogue);
     orc_store(out_dtype, out, e, y);
     if (Y) Y[e] = y;
   }

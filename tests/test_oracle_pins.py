@@ -337,7 +337,10 @@ def test_bad_arguments_are_rejected():
     with pytest.raises(ValueError):
         oracle.gemm(np.zeros(4, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, 3, F32, EPI_NONE)
     with pytest.raises(ValueError):
-        oracle.gemm(np.zeros(4, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F16, F32, 5)
+        oracle.gemm(np.zeros(4, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F16, F32, 6)
+    with pytest.raises(ValueError):
+        oracle.gemm(np.zeros(4, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F16, F32, EPI_NONE,
+                    bias=np.zeros(3, np.float32))
     with pytest.raises(ValueError):
         oracle.gemm(np.zeros(3, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F16, F32, EPI_NONE)
 
