@@ -34,7 +34,7 @@ import numpy as np
 import torch
 
 F32, F16, BF16 = 0, 4, 5
-EPI_NONE, EPI_RELU = 0, 1
+EPI_NONE, EPI_RELU, EPI_GELU, EPI_GELU_ERF, EPI_SIGMOID, EPI_TANH = 0, 1, 2, 3, 4, 5
 
 TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
 DTYPE_NAME = {F32: "f32", F16: "f16", BF16: "bf16"}
@@ -132,9 +132,20 @@ def make_inputs(w: Workload, seed: int | None = None):
 def custom(M, N, K, in_dtype=F16, out_dtype=F32, epilogue=EPI_RELU, dist=NORMAL, seed=0,
            batch=1, dist_b=None, name=None) -> Workload:
     """A small workload for parity cases (same drawing rules as the five)."""
-    exact = dist.kind == "randint" and (dist_b or dist).kind == "randint"
+    exact = (dist.kind == "randint" and (dist_b or dist).kind == "randint"
+             and epilogue in (EPI_NONE, EPI_RELU))
     return Workload(name or f"custom_{M}x{N}x{K}", M, N, K, in_dtype, out_dtype, epilogue, seed,
                     dist, dist_b or dist, batch=batch, exact=exact)
+
+
+def draw_bias(N: int, dist: Dist, seed: int) -> torch.Tensor:
+    """A bias row of N fp32 values (not rounded to a 16-bit type)."""
+    gen = torch.Generator().manual_seed(seed)
+    if dist.kind == "normal":
+        return torch.randn(N, generator=gen, dtype=torch.float32) * dist.b + dist.a
+    if dist.kind == "randint":
+        return torch.randint(int(dist.a), int(dist.b) + 1, (N,), generator=gen).to(torch.float32)
+    return torch.rand(N, generator=gen, dtype=torch.float32) * (dist.b - dist.a) + dist.a
 
 
 def sample_indices(M: int, N: int, count: int, seed: int, batch: int = 1):

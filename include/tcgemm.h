@@ -8,8 +8,18 @@
  * Tile.dot, Tile.relu, Tile.to, In.at, Out.put):
  *
  *     acc = +0, then acc += A[b,i,k] * B[b,k,j] for k = 0 .. K-1, in fp32
- *     y   = relu ? (acc > 0 ? acc : +0) : acc
+ *     v   = bias ? acc + bias[j] : acc                    (Tile.add, broadcast)
+ *     y   = act(v)   (none, relu, gelu, geluErf, sigmoid or tanh, in fp32)
  *     C[b,i,j] = y rounded to nearest-even in the output storage type
+ *
+ * With a split K (desc.split_k > 1, or GEMM_FLAG_SPLIT_K and the planner's
+ * choice) the K range is cut into split_k consecutive ranges of whole trips;
+ * each range's sum is formed as above and the ranges' sums are then added in
+ * ascending order in fp32 before the epilogue.  This reassociates the fold:
+ * the result is exact wherever every partial sum is exact (integer inputs
+ * whose sums stay below 2^24) and otherwise differs from the unsplit fold by
+ * rounding only.  Every path of one plan (staged, one stage, unstaged)
+ * splits the same way and returns the same bits.
  *
  * Elements outside the matrices read as 0 (In.at) and elements outside C are
  * never written (Out.put: "the rest keeps its values").  The staged kernel
@@ -43,8 +53,23 @@ extern "C" {
 /* Storage codes (page "gizml:tile", Constants). */
 enum { GEMM_F32 = 0, GEMM_F16 = 4, GEMM_BF16 = 5 };
 
-/* Epilogues: none, or max(y, 0) with NaN and -0 giving +0 (Tile.relu). */
-enum { GEMM_EPI_NONE = 0, GEMM_EPI_RELU = 1 };
+/* Activations applied after the optional bias (page "gizml:tile": Tile.relu,
+ * Tile.gelu, Tile.geluErf, Tile.sigmoid, Tile.tanh):
+ *   RELU      max(v, 0), with NaN and -0 giving +0
+ *   GELU      the tanh form: v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))) / 2
+ *   GELU_ERF  the erf form:  v (1 + erf(v / sqrt(2))) / 2
+ *   SIGMOID   1 / (1 + e^-v)
+ *   TANH      tanh(v)
+ * The transcendental ones are evaluated in fp32 with the device math
+ * library (a few ulp), then rounded to the output type. */
+enum {
+  GEMM_EPI_NONE = 0,
+  GEMM_EPI_RELU = 1,
+  GEMM_EPI_GELU = 2,
+  GEMM_EPI_GELU_ERF = 3,
+  GEMM_EPI_SIGMOID = 4,
+  GEMM_EPI_TANH = 5
+};
 
 /* Plan flags.
  *   GEMM_FLAG_FORCE_STAGES_1: use at most one LDS stage even where two fit.
@@ -52,8 +77,20 @@ enum { GEMM_EPI_NONE = 0, GEMM_EPI_RELU = 1 };
  *     global memory (the "Setting.stage off" case of the page "Module
  *     Tolk.Stage", depth).
  *   GEMM_FLAG_FORCE_STAGES_2: use at most two stages even where the tile's
- *     kernel could keep more chunks in flight. */
-enum { GEMM_FLAG_FORCE_STAGES_1 = 1, GEMM_FLAG_UNSTAGED = 2, GEMM_FLAG_FORCE_STAGES_2 = 4 };
+ *     kernel could keep more chunks in flight.
+ *   GEMM_FLAG_BIAS: add a bias row before the activation: N fp32 values,
+ *     bias[j] added to column j of every row of every batch item (passed
+ *     to gemm_run_ex).
+ *   GEMM_FLAG_SPLIT_K: with split_k == 0, let the planner split K where
+ *     that is estimated faster (few output tiles, long K); such a plan
+ *     needs a workspace (gemm_plan_info.workspace_bytes). */
+enum {
+  GEMM_FLAG_FORCE_STAGES_1 = 1,
+  GEMM_FLAG_UNSTAGED = 2,
+  GEMM_FLAG_FORCE_STAGES_2 = 4,
+  GEMM_FLAG_BIAS = 8,
+  GEMM_FLAG_SPLIT_K = 16
+};
 
 /* Error codes. */
 enum {
@@ -67,23 +104,27 @@ enum {
   GEMM_E_LAUNCH = -6,  /* the kernel launch failed (hipGetLastError)           */
   GEMM_E_NOMEM = -7,   /* host allocation of the plan failed                   */
   GEMM_E_PLAN = -8,    /* null or destroyed plan                               */
-  GEMM_E_SIZE = -9     /* a tile's byte offsets would not fit 31 bits          */
+  GEMM_E_SIZE = -9,    /* a tile's byte offsets would not fit 31 bits          */
+  GEMM_E_WORKSPACE = -10 /* the plan needs a workspace (split K) and none, a
+                            smaller or a misaligned one was given             */
 };
 
 /* The problem.  M, N >= 0, K >= 0 (K == 0 gives C = epilogue(+0));
  * batch >= 1; with batch > 1, stride_a >= M*K, stride_b >= K*N and
  * stride_c >= M*N.  `tile` selects a tile configuration by id (1 ..
- * gemm_tile_count()), or 0 for the planner's choice. */
+ * gemm_tile_count()), or 0 for the planner's choice.  `split_k` cuts K into
+ * that many ranges (1 .. 256; fewer if K has fewer trips), or 0 for one
+ * range unless GEMM_FLAG_SPLIT_K lets the planner choose. */
 typedef struct gemm_desc {
   int64_t M, N, K;
   int32_t in_dtype;  /* GEMM_F16 or GEMM_BF16 (A and B)      */
   int32_t out_dtype; /* GEMM_F32, GEMM_F16 or GEMM_BF16 (C)   */
-  int32_t epilogue;  /* GEMM_EPI_NONE or GEMM_EPI_RELU         */
+  int32_t epilogue;  /* GEMM_EPI_* activation                   */
   int32_t flags;     /* GEMM_FLAG_* bits                       */
   int64_t batch;
   int64_t stride_a, stride_b, stride_c;
   int32_t tile;
-  int32_t reserved; /* must be 0 */
+  int32_t split_k;
 } gemm_desc;
 
 /* What the planner needs to know about a device (page "Module Tolk.Stage":
@@ -107,11 +148,13 @@ typedef struct gemm_plan_info {
   int32_t lds_bytes;        /* LDS the kernel declares                       */
   int32_t vec16;            /* 1: 16-byte copies; 0: element copies          */
   int64_t tiles_m, tiles_n; /* output tiles along M and N                    */
-  int64_t workgroups;       /* tiles_m * tiles_n * batch                     */
+  int64_t workgroups;       /* tiles_m * tiles_n * batch * split_k           */
   int64_t trips;            /* K-trips: ceil(K / bk)                         */
   int64_t mfma_per_run;     /* MFMA instructions one run issues              */
   int32_t mfma_m, mfma_n, mfma_k;
-  int32_t reserved;
+  int32_t split_k;          /* K ranges (1: no split)                        */
+  int64_t trips_per_split;  /* trips of each K range (the last may have fewer) */
+  int64_t workspace_bytes;  /* device workspace a run needs (0 without split) */
 } gemm_plan_info;
 
 typedef struct gemm_plan_s* gemm_plan_t;
@@ -132,6 +175,19 @@ int gemm_plan_get_info(gemm_plan_t plan, gemm_plan_info* out);
  * string belongs to the plan. */
 const char* gemm_plan_describe(gemm_plan_t plan);
 
+/* Extra arguments of a run.  bias: device pointer to N fp32 values, needed
+ * by plans made with GEMM_FLAG_BIAS (else ignored).  workspace: device
+ * memory of at least gemm_plan_info.workspace_bytes bytes, 256-byte aligned,
+ * needed by split-K plans (else ignored); its contents on entry do not
+ * matter and are overwritten; two runs in flight at once need two
+ * workspaces.  Neither may overlap A, B or C. */
+typedef struct gemm_run_args {
+  const void* bias;
+  void* workspace;
+  int64_t workspace_bytes;
+  int64_t reserved[4]; /* must be 0 */
+} gemm_run_args;
+
 /*
  * Launch C = epilogue(A . B) on `stream` (a hipStream_t; NULL = the null
  * stream).  A, B, C are device pointers owned by the caller, aligned to
@@ -143,6 +199,20 @@ const char* gemm_plan_describe(gemm_plan_t plan);
  * GEMM_E_LAUNCH if the launch fails.  M == 0 or N == 0 launches nothing.
  */
 int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream);
+
+/*
+ * gemm_run with a bias and a workspace (args may be NULL for plans that
+ * need neither).  A split-K plan launches two kernels on `stream`: the GEMM,
+ * which writes each K range's fp32 sums into the workspace, then the
+ * reduction, which writes C.  Returns GEMM_E_ARG if the plan needs a bias
+ * and none is given (or args->reserved is not 0), GEMM_E_WORKSPACE if it
+ * needs a workspace and none, a smaller or a misaligned one is given,
+ * GEMM_E_ALIAS if the bias or workspace overlaps A, B or C, and otherwise
+ * what gemm_run returns.  gemm_run(plan, ...) is gemm_run_ex(plan, ...,
+ * NULL, stream).
+ */
+int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void* C, const gemm_run_args* args,
+                void* stream);
 
 /* Free a plan (NULL is ignored). */
 void gemm_plan_destroy(gemm_plan_t plan);

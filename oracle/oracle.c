@@ -24,7 +24,9 @@
  * follow their definitions on the page, evaluated in double precision from
  * the fp32 value v and rounded once to fp32 (the page asks for results
  * within a few ulp; this is the correctly rounded value up to double's own
- * error):
+ * error, except far in the negative tail of the two GELU forms, where
+ * 1 + tanh and 1 + erf cancel in double and leave an absolute error of
+ * about 1e-16 |v| on results that small):
  *     relu(v)    = v > 0 ? v : +0
  *     gelu(v)    = v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3)))   (tanh form)
  *     geluErf(v) = v/2 * (1 + erf(v / sqrt(2)))                          (erf form)

@@ -10,15 +10,15 @@ from __future__ import annotations
 
 import torch
 
-from .capi import (BF16, EPI_NONE, EPI_RELU, F16, F32, FLAG_FORCE_STAGES_1, FLAG_FORCE_STAGES_2,
-                   FLAG_UNSTAGED,
-                   GEMM_E_ALIAS, GEMM_E_ALIGN, GEMM_E_ARG, GEMM_E_DEVICE, GEMM_E_DTYPE,
-                   GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE, GEMM_OK, CODE_TO_TORCH,
-                   TORCH_TO_CODE, GemmError, Plan, check_runtime, gemm_desc, gemm_device_caps,
-                   gemm_device_caps_query, gemm_plan, gemm_plan_describe, gemm_plan_destroy,
-                   gemm_plan_for_caps, gemm_plan_get_info, gemm_plan_info, gemm_run,
-                   gemm_runtime_version, gemm_stage_depth, gemm_strerror, gemm_tile_count,
-                   make_caps, make_desc)
+from .capi import (BF16, EPI_GELU, EPI_GELU_ERF, EPI_NONE, EPI_RELU, EPI_SIGMOID, EPI_TANH, F16,
+                   F32, FLAG_BIAS, FLAG_FORCE_STAGES_1, FLAG_FORCE_STAGES_2, FLAG_SPLIT_K,
+                   FLAG_UNSTAGED, GEMM_E_ALIAS, GEMM_E_ALIGN, GEMM_E_ARG, GEMM_E_DEVICE,
+                   GEMM_E_DTYPE, GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE,
+                   GEMM_E_WORKSPACE, GEMM_OK, CODE_TO_TORCH, TORCH_TO_CODE, GemmError, Plan,
+                   check_runtime, gemm_desc, gemm_device_caps, gemm_device_caps_query, gemm_plan,
+                   gemm_plan_describe, gemm_plan_destroy, gemm_plan_for_caps, gemm_plan_get_info,
+                   gemm_plan_info, gemm_run, gemm_run_args, gemm_run_ex, gemm_runtime_version,
+                   gemm_stage_depth, gemm_strerror, gemm_tile_count, make_caps, make_desc)
 from ._lib import LIB_PATH, lib
 
 lib()  # fail loudly now if the library is missing
@@ -27,26 +27,34 @@ _plan_cache: dict = {}
 
 
 def plan_for(M, N, K, in_dtype, out_dtype, epilogue=EPI_NONE, flags=0, batch=1, stride_a=0,
-             stride_b=0, stride_c=0, tile=0) -> Plan:
+             stride_b=0, stride_c=0, tile=0, split_k=0) -> Plan:
     """A cached plan for the current device (plans are immutable)."""
     key = (torch.cuda.current_device(), M, N, K, in_dtype, out_dtype, epilogue, flags, batch,
-           stride_a, stride_b, stride_c, tile)
+           stride_a, stride_b, stride_c, tile, split_k)
     p = _plan_cache.get(key)
     if p is None:
         p = gemm_plan(make_desc(M, N, K, in_dtype, out_dtype, epilogue, flags, batch, stride_a,
-                                stride_b, stride_c, tile))
+                                stride_b, stride_c, tile, split_k))
         _plan_cache[key] = p
     return p
 
 
-def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, out_dtype=None,
-           out: torch.Tensor | None = None, flags: int = 0, tile: int = 0,
-           stream=None) -> torch.Tensor:
-    """C = relu?(A @ B) with fp32 accumulation on the MFMA units.
+_ACT = {None: EPI_NONE, "none": EPI_NONE, "relu": EPI_RELU, "gelu": EPI_GELU,
+        "gelu_erf": EPI_GELU_ERF, "sigmoid": EPI_SIGMOID, "tanh": EPI_TANH}
+
+
+def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | None = None,
+           bias: torch.Tensor | None = None, out_dtype=None, out: torch.Tensor | None = None,
+           flags: int = 0, tile: int = 0, split_k: int = 0, stream=None) -> torch.Tensor:
+    """C = act(A @ B + bias) with fp32 accumulation on the MFMA units.
 
     A is [M, K] or [batch, M, K], B is [K, N] or [batch, K, N]; both fp16 or
-    both bf16, row-major and contiguous, on the GPU.  out_dtype is
-    torch.float32, float16 or bfloat16 (default: the input type).
+    both bf16, row-major and contiguous, on the GPU.  bias is an fp32 vector
+    of N values (one per column, shared by every row and batch item).  act is
+    None, "relu", "gelu" (tanh form), "gelu_erf", "sigmoid" or "tanh"
+    (relu=True means act="relu").  out_dtype is torch.float32, float16 or
+    bfloat16 (default: the input type).  split_k > 1 (or flags with
+    FLAG_SPLIT_K) splits K; the workspace comes from torch's allocator.
     """
     if A.dtype not in (torch.float16, torch.bfloat16) or B.dtype != A.dtype:
         raise TypeError("A and B must share one dtype, float16 or bfloat16")
@@ -66,17 +74,33 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, out_dtype=No
     odt = out_dtype or A.dtype
     if odt not in TORCH_TO_CODE:
         raise TypeError("out_dtype must be float32, float16 or bfloat16")
+    if act not in _ACT:
+        raise ValueError(f"unknown activation {act!r}")
+    epi = EPI_RELU if relu and act is None else _ACT[act]
+    if relu and act not in (None, "relu"):
+        raise ValueError("relu=True conflicts with act")
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.numel() != N or not bias.is_contiguous() \
+                or bias.device != A.device:
+            raise ValueError("bias must be a contiguous float32 vector of N values on A's device")
+        flags |= FLAG_BIAS
     shape = (batch, M, N) if A.dim() == 3 else (M, N)
     if out is None:
         out = torch.empty(shape, dtype=odt, device=A.device)
     elif tuple(out.shape) != shape or out.dtype != odt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
     with torch.cuda.device(A.device):
-        p = plan_for(M, N, K, TORCH_TO_CODE[A.dtype], TORCH_TO_CODE[odt],
-                     EPI_RELU if relu else EPI_NONE, flags, batch,
+        p = plan_for(M, N, K, TORCH_TO_CODE[A.dtype], TORCH_TO_CODE[odt], epi, flags, batch,
                      M * K if batch > 1 else 0, K * N if batch > 1 else 0,
-                     M * N if batch > 1 else 0, tile)
-        gemm_run(p, A, B, out, stream)
+                     M * N if batch > 1 else 0, tile, split_k)
+        ws_bytes = p.info().workspace_bytes
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device) if ws_bytes else None
+        gemm_run_ex(p, A, B, out, bias=bias, workspace=ws, stream=stream)
+        if ws is not None and stream is not None:
+            # the workspace was allocated for torch's current stream
+            if isinstance(stream, int):
+                raise ValueError("a split-K run on a raw stream needs gemm_run_ex with a workspace")
+            ws.record_stream(stream)
     return out
 
 

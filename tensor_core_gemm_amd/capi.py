@@ -14,12 +14,13 @@ import torch
 from ._lib import lib
 
 F32, F16, BF16 = 0, 4, 5
-EPI_NONE, EPI_RELU = 0, 1
-FLAG_FORCE_STAGES_1, FLAG_UNSTAGED, FLAG_FORCE_STAGES_2 = 1, 2, 4
+EPI_NONE, EPI_RELU, EPI_GELU, EPI_GELU_ERF, EPI_SIGMOID, EPI_TANH = 0, 1, 2, 3, 4, 5
+FLAG_FORCE_STAGES_1, FLAG_UNSTAGED, FLAG_FORCE_STAGES_2, FLAG_BIAS, FLAG_SPLIT_K = 1, 2, 4, 8, 16
 
 GEMM_OK = 0
 GEMM_E_ARG, GEMM_E_DTYPE, GEMM_E_ALIGN, GEMM_E_ALIAS = -1, -2, -3, -4
 GEMM_E_DEVICE, GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE = -5, -6, -7, -8, -9
+GEMM_E_WORKSPACE = -10
 
 TORCH_TO_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 CODE_TO_TORCH = {v: k for k, v in TORCH_TO_CODE.items()}
@@ -31,7 +32,7 @@ class gemm_desc(ctypes.Structure):
                 ("epilogue", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("batch", ctypes.c_int64), ("stride_a", ctypes.c_int64),
                 ("stride_b", ctypes.c_int64), ("stride_c", ctypes.c_int64),
-                ("tile", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32)]
 
 
 class gemm_device_caps(ctypes.Structure):
@@ -49,10 +50,16 @@ class gemm_plan_info(ctypes.Structure):
                 ("workgroups", ctypes.c_int64), ("trips", ctypes.c_int64),
                 ("mfma_per_run", ctypes.c_int64), ("mfma_m", ctypes.c_int32),
                 ("mfma_n", ctypes.c_int32), ("mfma_k", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("trips_per_split", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class gemm_run_args(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_int64), ("reserved", ctypes.c_int64 * 4)]
 
 
 _vp = ctypes.c_void_p
@@ -64,6 +71,7 @@ _SIGS = {
     "gemm_plan_get_info": (ctypes.c_int, [_vp, ctypes.POINTER(gemm_plan_info)]),
     "gemm_plan_describe": (ctypes.c_char_p, [_vp]),
     "gemm_run": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
+    "gemm_run_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_void_p, _vp]),
     "gemm_plan_destroy": (None, [_vp]),
     "gemm_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gemm_stage_depth": (ctypes.c_int, [ctypes.POINTER(gemm_device_caps), ctypes.c_int64,
@@ -125,9 +133,9 @@ def gemm_stage_depth(caps: gemm_device_caps, used: int, tile_bytes, stage_enable
 
 
 def make_desc(M, N, K, in_dtype=F16, out_dtype=F32, epilogue=EPI_NONE, flags=0, batch=1,
-              stride_a=0, stride_b=0, stride_c=0, tile=0) -> gemm_desc:
+              stride_a=0, stride_b=0, stride_c=0, tile=0, split_k=0) -> gemm_desc:
     return gemm_desc(M, N, K, in_dtype, out_dtype, epilogue, flags, batch, stride_a, stride_b,
-                     stride_c, tile, 0)
+                     stride_c, tile, split_k)
 
 
 class Plan:
@@ -194,17 +202,33 @@ def _ptr(x) -> int | None:
     return x.data_ptr()
 
 
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
 def gemm_run(plan: Plan, A, B, C, stream=None) -> None:
     """Launch on `stream` (a torch.cuda.Stream, a raw hipStream_t int, or
     None for torch's current stream).  A, B, C are device tensors or raw
     device pointers; nothing is synchronised."""
-    if stream is None:
-        s = torch.cuda.current_stream().cuda_stream
-    elif isinstance(stream, int):
-        s = stream
-    else:
-        s = stream.cuda_stream
-    _check(_fn("gemm_run")(plan.handle, _ptr(A), _ptr(B), _ptr(C), s), "gemm_run")
+    _check(_fn("gemm_run")(plan.handle, _ptr(A), _ptr(B), _ptr(C), _stream(stream)), "gemm_run")
+
+
+def gemm_run_ex(plan: Plan, A, B, C, bias=None, workspace=None, workspace_bytes=None,
+                stream=None) -> None:
+    """gemm_run with a bias (N fp32 values on the device) and a workspace
+    (device memory of at least the plan's workspace_bytes, 256-byte aligned);
+    tensors or raw device pointers."""
+    if workspace_bytes is None:
+        workspace_bytes = 0
+        if workspace is not None and not isinstance(workspace, int):
+            workspace_bytes = workspace.numel() * workspace.element_size()
+    args = gemm_run_args(_ptr(bias), _ptr(workspace), workspace_bytes)
+    _check(_fn("gemm_run_ex")(plan.handle, _ptr(A), _ptr(B), _ptr(C), ctypes.byref(args),
+                              _stream(stream)), "gemm_run_ex")
 
 
 def check_runtime() -> None:

@@ -17,6 +17,7 @@
 namespace {
 
 constexpr uint32_t kPlanMagic = 0x7C6E3A11u;
+constexpr int kMaxSplits = 256;
 
 struct Plan {
   uint32_t magic;
@@ -24,7 +25,7 @@ struct Plan {
   gemm_plan_info info;
   int32_t group_m;
   int32_t xcd_remap;
-  char text[320];
+  char text[400];
 };
 
 bool log_enabled() {
@@ -67,10 +68,12 @@ int validate_desc(const gemm_desc* d) {
   if (d->in_dtype != GEMM_F16 && d->in_dtype != GEMM_BF16) return GEMM_E_DTYPE;
   if (d->out_dtype != GEMM_F32 && d->out_dtype != GEMM_F16 && d->out_dtype != GEMM_BF16)
     return GEMM_E_DTYPE;
-  if (d->epilogue != GEMM_EPI_NONE && d->epilogue != GEMM_EPI_RELU) return GEMM_E_ARG;
-  if (d->flags & ~(GEMM_FLAG_FORCE_STAGES_1 | GEMM_FLAG_UNSTAGED | GEMM_FLAG_FORCE_STAGES_2)) return GEMM_E_ARG;
+  if (d->epilogue < GEMM_EPI_NONE || d->epilogue > GEMM_EPI_TANH) return GEMM_E_ARG;
+  if (d->flags & ~(GEMM_FLAG_FORCE_STAGES_1 | GEMM_FLAG_UNSTAGED | GEMM_FLAG_FORCE_STAGES_2 |
+                   GEMM_FLAG_BIAS | GEMM_FLAG_SPLIT_K))
+    return GEMM_E_ARG;
   if (d->tile < 0 || d->tile > tcg::kNumTiles) return GEMM_E_ARG;
-  if (d->reserved != 0) return GEMM_E_ARG;
+  if (d->split_k < 0 || d->split_k > kMaxSplits) return GEMM_E_ARG;
   if (d->batch > 1) {
     if (d->stride_a < d->M * d->K || d->stride_b < d->K * d->N || d->stride_c < d->M * d->N)
       return GEMM_E_ARG;
@@ -91,28 +94,67 @@ double tile_efficiency(int id) {
   }
 }
 
-// Choose a tile for the problem: short-K products whose N is a multiple of
-// 96 take the 256 x 96 tile (few trips, many workgroups to stream A and C;
-// measured faster than one 128 x 288 tile per row block); the rest take the
-// general tile with the lowest estimated time: the busiest CU's tiles
-// (workgroups are spread over all CUs) times one tile's MFMA work over the
-// tile's efficiency.  The deeper-ring tiles (6, 7) are selected by id.
-int choose_tile(const gemm_desc& d, const gemm_device_caps& caps) {
-  if (d.K <= 128 && d.N > 0 && d.N % 96 == 0) return 4;
-  int best = 1;
+// Time model of the planner, in microseconds, calibrated on MI355X under
+// sustained load: one 256 x 256 x 64 trip of the first tile takes about
+// kTrip1Us with every CU busy; a workgroup also spends about one trip on its
+// prologue and epilogue; workgroups run one per CU; a split-K run adds its
+// reduction, which moves every partial sum twice (written by the GEMM, read
+// back) at an effective kReduceBytesPerUs, plus one launch.  The partial
+// sums mostly stay in the last-level cache: 2048 x 2048 x 16384 in four
+// ranges measured 134 us against 120 us for the same work unsplit, which
+// puts the effective rate near 10 TB/s.
+constexpr double kTrip1Us = 2.0;
+constexpr double kReduceBytesPerUs = 10.0e6;
+constexpr double kLaunchUs = 4.0;
+
+double estimate_us(const gemm_desc& d, const gemm_device_caps& caps, int id, int64_t splits) {
+  const auto& t = tile_desc(id);
+  const int64_t trips = std::max<int64_t>(cdiv(d.K, t.bk), 1);
+  const int64_t tps = cdiv(trips, splits);
+  const int64_t ranges = cdiv(trips, tps);
+  const int64_t wgs = cdiv(d.M, t.bm) * cdiv(d.N, t.bn) * d.batch * ranges;
+  const int64_t rounds = cdiv(std::max<int64_t>(wgs, 1), std::max(caps.num_cus, 1));
+  const double trip_us = kTrip1Us * ((double)t.bm * t.bn * t.bk / (256.0 * 256.0 * 64.0)) / tile_efficiency(id);
+  double us = (double)rounds * (double)(tps + 1) * trip_us;
+  if (ranges > 1) {
+    const double mn = (double)d.M * (double)d.N * (double)d.batch;
+    us += (2.0 * ranges * mn * 4.0 + mn * out_size(d.out_dtype)) / kReduceBytesPerUs + kLaunchUs;
+  }
+  return us;
+}
+
+// Split counts the planner considers: powers of two while every range keeps
+// at least kMinTripsPerSplit trips.
+constexpr int64_t kMinTripsPerSplit = 8;
+
+// Choose a tile (and, where allowed, a split) for the problem: short-K
+// products whose N is a multiple of 96 take the 256 x 96 tile (few trips,
+// many workgroups to stream A and C; measured faster than one 128 x 288 tile
+// per row block); the rest take the general tile and split with the lowest
+// estimated time.  The deeper-ring tiles (6, 7) are selected by id.
+void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, int* tile, int64_t* splits) {
+  *splits = 1;
+  if (d.tile) {
+    *tile = d.tile;
+    if (!may_split) return;
+  } else if (d.K <= 128 && d.N > 0 && d.N % 96 == 0) {
+    *tile = 4;
+    return;
+  }
   double best_t = 1e300;
-  for (int id = 1; id <= 3; ++id) {
-    const auto& t = tile_desc(id);
-    const int64_t tiles = cdiv(d.M, t.bm) * cdiv(d.N, t.bn) * d.batch;
-    const int64_t per_cu = cdiv(std::max<int64_t>(tiles, 1), std::max(caps.num_cus, 1));
-    const double work = (double)t.bm * t.bn * (double)(cdiv(std::max<int64_t>(d.K, 1), t.bk) * t.bk);
-    const double est = (double)per_cu * work / tile_efficiency(id);
-    if (est < best_t * 0.999) {
-      best_t = est;
-      best = id;
+  const int lo = d.tile ? d.tile : 1, hi = d.tile ? d.tile : 3;
+  for (int id = lo; id <= hi; ++id) {
+    const int64_t trips = cdiv(d.K, tile_desc(id).bk);
+    for (int64_t sp = 1; sp <= kMaxSplits; sp *= 2) {
+      if (sp > 1 && (!may_split || trips / sp < kMinTripsPerSplit)) break;
+      const double est = estimate_us(d, caps, id, sp);
+      if (est < best_t * 0.999) {
+        best_t = est;
+        *tile = id;
+        *splits = sp;
+      }
     }
   }
-  return best;
 }
 
 }  // namespace
@@ -130,6 +172,7 @@ extern "C" const char* gemm_strerror(int code) {
     case GEMM_E_NOMEM: return "host allocation failed";
     case GEMM_E_PLAN: return "null or destroyed plan";
     case GEMM_E_SIZE: return "problem too large: a tile's byte offsets exceed 31 bits";
+    case GEMM_E_WORKSPACE: return "the plan splits K and needs a larger or 256-byte aligned workspace";
     default: return "unknown error code";
   }
 }
@@ -199,7 +242,14 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
     d.stride_b = d.K * d.N;
     d.stride_c = d.M * d.N;
   }
-  const int id = d.tile ? d.tile : choose_tile(d, *caps);
+  int id = 0;
+  int64_t want_splits = 1;
+  if (d.split_k > 0) {
+    choose(d, *caps, false, &id, &want_splits);
+    want_splits = d.split_k;
+  } else {
+    choose(d, *caps, (d.flags & GEMM_FLAG_SPLIT_K) != 0, &id, &want_splits);
+  }
   const auto& t = tile_desc(id);
 
   const int64_t tiles[2] = {(int64_t)t.bm * t.bk * 2, (int64_t)t.bk * t.bn * 2};
@@ -213,14 +263,24 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
   }
   if ((d.flags & GEMM_FLAG_FORCE_STAGES_1) && stages > 1) stages = 1;
 
+  // The first slot also holds the epilogue bands, which can be larger than
+  // a slot for small tiles; even the unstaged kernel needs the bands.
+  while (stages > 0 && tcg::lds_bytes_for(t, stages) > caps->lds_bytes) --stages;
+  if (tcg::lds_bytes_for(t, stages) > caps->lds_bytes) return GEMM_E_DEVICE;
   // Byte offsets inside one trip's tiles are 32-bit buffer offsets.
   if ((int64_t)t.bm * std::max<int64_t>(d.K, 1) * 2 >= (int64_t)0x7fffffff ||
       (int64_t)t.bk * std::max<int64_t>(d.N, 1) * 2 >= (int64_t)0x7fffffff)
     return GEMM_E_SIZE;
   const int64_t tiles_m = cdiv(d.M, t.bm), tiles_n = cdiv(d.N, t.bn);
-  const int64_t wgs = tiles_m * tiles_n * d.batch;
+  const int64_t trips = cdiv(d.K, t.bk);
+  // K ranges of whole trips; none empty (K == 0 keeps one range).
+  const bool can_split = trips > 0 && d.M > 0 && d.N > 0;
+  const int64_t tps = can_split ? cdiv(trips, std::min<int64_t>(want_splits, trips)) : trips;
+  const int64_t splits = can_split ? cdiv(trips, tps) : 1;
+  const int64_t wgs = tiles_m * tiles_n * d.batch * splits;
   const int nt = t.wm * t.wn * 64;
-  if (wgs * nt >= ((int64_t)1 << 32) || cdiv(d.K, t.bk) > 0x7fffffff) return GEMM_E_SIZE;
+  if (wgs * nt >= ((int64_t)1 << 32) || trips > 0x7fffffff) return GEMM_E_SIZE;
+  const int64_t ws_bytes = splits > 1 ? splits * d.batch * d.M * d.N * 4 : 0;
 
   Plan* p = new (std::nothrow) Plan();
   if (!p) return GEMM_E_NOMEM;
@@ -233,26 +293,35 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
   in.bk = t.bk;
   in.waves = t.wm * t.wn;
   in.stages = stages;
-  in.lds_bytes = stages == 0 ? 0 : (int32_t)(stages * (tiles[0] + tiles[1]));
+  in.lds_bytes = tcg::lds_bytes_for(t, stages);
   in.vec16 = (d.K % 8 == 0 && d.N % 8 == 0 && d.stride_a % 8 == 0 && d.stride_b % 8 == 0) ? 1 : 0;
   in.tiles_m = tiles_m;
   in.tiles_n = tiles_n;
   in.workgroups = wgs;
-  in.trips = cdiv(d.K, t.bk);
+  in.trips = trips;
   const int fm = t.bm / t.wm / tcg::kMfmaM, fn = t.bn / t.wn / tcg::kMfmaN;
-  in.mfma_per_run = wgs * in.waves * fm * fn * in.trips * (t.bk / tcg::kMfmaK);
+  in.mfma_per_run = tiles_m * tiles_n * d.batch * in.waves * fm * fn * in.trips * (t.bk / tcg::kMfmaK);
   in.mfma_m = tcg::kMfmaM;
   in.mfma_n = tcg::kMfmaN;
   in.mfma_k = tcg::kMfmaK;
+  in.split_k = (int32_t)splits;
+  in.trips_per_split = tps;
+  in.workspace_bytes = ws_bytes;
   p->group_m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(4, tiles_m));
   p->xcd_remap = caps->num_xcds == 8 ? 1 : 0;
+  static const char* const kActName[] = {"none", "relu", "gelu", "gelu_erf", "sigmoid", "tanh"};
+  char split_text[96] = "";
+  if (splits > 1)
+    std::snprintf(split_text, sizeof(split_text), ", split K %lld x %lld trips (workspace %lld B)",
+                  (long long)splits, (long long)tps, (long long)ws_bytes);
   std::snprintf(p->text, sizeof(p->text),
-                "tile %d (%dx%dx%d, %d waves), stages %d, LDS %d B, %s copies, grid %lld (%lldx%lld x %lld), "
-                "trips %lld, mfma %dx%dx%d %s, %lld MFMAs",
+                "tile %d (%dx%dx%d, %d waves), stages %d, LDS %d B, %s copies, grid %lld (%lldx%lld x %lld%s), "
+                "trips %lld, mfma %dx%dx%d %s, %lld MFMAs, epilogue %s%s%s",
                 id, t.bm, t.bn, t.bk, in.waves, stages, in.lds_bytes, in.vec16 ? "16-byte" : "element",
                 (long long)wgs, (long long)tiles_m, (long long)tiles_n, (long long)d.batch,
-                (long long)in.trips, in.mfma_m, in.mfma_n, in.mfma_k,
-                d.in_dtype == GEMM_BF16 ? "bf16" : "f16", (long long)in.mfma_per_run);
+                splits > 1 ? " x splits" : "", (long long)in.trips, in.mfma_m, in.mfma_n, in.mfma_k,
+                d.in_dtype == GEMM_BF16 ? "bf16" : "f16", (long long)in.mfma_per_run,
+                (d.flags & GEMM_FLAG_BIAS) ? "bias+" : "", kActName[d.epilogue], split_text);
   if (log_enabled()) std::fprintf(stderr, "[tcgemm] plan %lldx%lldx%lld: %s\n", (long long)d.M,
                                   (long long)d.N, (long long)d.K, p->text);
   *out = reinterpret_cast<gemm_plan_t>(p);
@@ -305,10 +374,28 @@ static bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
 }
 
 extern "C" int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream) {
+  return gemm_run_ex(plan, A, B, C, nullptr, stream);
+}
+
+extern "C" int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void* C, const gemm_run_args* args,
+                           void* stream) {
   Plan* p = as_plan(plan);
   if (!p) return GEMM_E_PLAN;
   const gemm_desc& d = p->d;
   const gemm_plan_info& in = p->info;
+  if (args && (args->reserved[0] | args->reserved[1] | args->reserved[2] | args->reserved[3]))
+    return GEMM_E_ARG;
+  const bool want_bias = (d.flags & GEMM_FLAG_BIAS) != 0;
+  const float* bias = want_bias && args ? static_cast<const float*>(args->bias) : nullptr;
+  if (want_bias && !bias) return GEMM_E_ARG;
+  if (bias && ((uintptr_t)bias & 3u)) return GEMM_E_ALIGN;
+  float* ws = nullptr;
+  if (in.split_k > 1) {
+    if (!args || !args->workspace || args->workspace_bytes < in.workspace_bytes ||
+        ((uintptr_t)args->workspace & 255u))
+      return GEMM_E_WORKSPACE;
+    ws = static_cast<float*>(args->workspace);
+  }
   if (d.M == 0 || d.N == 0) return GEMM_OK;
   if (!C || (d.K > 0 && (!A || !B))) return GEMM_E_ARG;
   const int osz = out_size(d.out_dtype);
@@ -321,7 +408,17 @@ extern "C" int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
     const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((d.batch - 1) * d.stride_a + d.M * d.K) * 2);
     const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((d.batch - 1) * d.stride_b + d.K * d.N) * 2);
     if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return GEMM_E_ALIAS;
+    if (ws) {
+      const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)in.workspace_bytes;
+      if (overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1)) return GEMM_E_ALIAS;
+    }
   }
+  if (bias) {
+    const uintptr_t z0 = (uintptr_t)bias, z1 = z0 + (uintptr_t)(d.N * 4);
+    if (overlaps(z0, z1, c0, c1)) return GEMM_E_ALIAS;
+    if (ws && overlaps(z0, z1, (uintptr_t)ws, (uintptr_t)ws + (uintptr_t)in.workspace_bytes)) return GEMM_E_ALIAS;
+  }
+  if (ws && overlaps((uintptr_t)ws, (uintptr_t)ws + (uintptr_t)in.workspace_bytes, c0, c1)) return GEMM_E_ALIAS;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
@@ -335,6 +432,8 @@ extern "C" int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
   a.A = static_cast<const uint16_t*>(A);
   a.B = static_cast<const uint16_t*>(B);
   a.C = C;
+  a.bias = bias;
+  a.ws = ws;
   a.M = d.M;
   a.N = d.N;
   a.K = d.K;
@@ -343,10 +442,14 @@ extern "C" int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
   a.stride_c = d.stride_c;
   a.tiles_m = in.tiles_m;
   a.tiles_n = in.tiles_n;
+  a.batch = d.batch;
   a.workgroups = in.workgroups;
   a.trips = (int32_t)in.trips;
+  a.splits = in.split_k;
+  a.trips_per_split = (int32_t)in.trips_per_split;
   a.out_dtype = d.out_dtype;
-  a.relu = d.epilogue == GEMM_EPI_RELU ? 1 : 0;
+  a.act = d.epilogue;
+  a.ws_vec = d.N % 4 == 0 ? 1 : 0;
   a.group_m = p->group_m;
   a.xcd_remap = p->xcd_remap;
   a.vec_store4 = (d.N % 4 == 0 && (c0 % (uintptr_t)(4 * osz)) == 0 && (d.batch == 1 || d.stride_c % 4 == 0)) ? 1 : 0;
@@ -356,15 +459,33 @@ extern "C" int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C,
   const bool bf16 = d.in_dtype == GEMM_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipErrorInvalidValue;
+  // The general epilogue's kernels only where the GEMM finishes C itself
+  // with a bias or a transcendental activation.
+  const bool gen = in.split_k == 1 && (bias || (d.epilogue != GEMM_EPI_NONE && d.epilogue != GEMM_EPI_RELU));
   switch (in.tile_id) {
-    case 1: e = tcg::launch_t1(in.stages, vec16, bf16, a, s); break;
-    case 2: e = tcg::launch_t2(in.stages, vec16, bf16, a, s); break;
-    case 3: e = tcg::launch_t3(in.stages, vec16, bf16, a, s); break;
-    case 4: e = tcg::launch_t4(in.stages, vec16, bf16, a, s); break;
-    case 5: e = tcg::launch_t5(in.stages, vec16, bf16, a, s); break;
-    case 6: e = tcg::launch_t6(in.stages, vec16, bf16, a, s); break;
-    case 7: e = tcg::launch_t7(in.stages, vec16, bf16, a, s); break;
+    case 1: e = (gen ? tcg::launch_t1_gen : tcg::launch_t1)(in.stages, vec16, bf16, a, s); break;
+    case 2: e = (gen ? tcg::launch_t2_gen : tcg::launch_t2)(in.stages, vec16, bf16, a, s); break;
+    case 3: e = (gen ? tcg::launch_t3_gen : tcg::launch_t3)(in.stages, vec16, bf16, a, s); break;
+    case 4: e = (gen ? tcg::launch_t4_gen : tcg::launch_t4)(in.stages, vec16, bf16, a, s); break;
+    case 5: e = (gen ? tcg::launch_t5_gen : tcg::launch_t5)(in.stages, vec16, bf16, a, s); break;
+    case 6: e = (gen ? tcg::launch_t6_gen : tcg::launch_t6)(in.stages, vec16, bf16, a, s); break;
+    case 7: e = (gen ? tcg::launch_t7_gen : tcg::launch_t7)(in.stages, vec16, bf16, a, s); break;
     default: break;
+  }
+  if (e == hipSuccess && in.split_k > 1) {
+    tcg::RArgs r;
+    r.ws = ws;
+    r.C = C;
+    r.bias = bias;
+    r.M = d.M;
+    r.N = d.N;
+    r.batch = d.batch;
+    r.stride_c = d.stride_c;
+    r.splits = in.split_k;
+    r.out_dtype = d.out_dtype;
+    r.act = d.epilogue;
+    r.vec4 = a.vec_store4;
+    e = tcg::launch_splitk_reduce(r, s);
   }
   if (e != hipSuccess) {
     if (log_enabled()) std::fprintf(stderr, "[tcgemm] launch failed: %s\n", hipGetErrorString(e));

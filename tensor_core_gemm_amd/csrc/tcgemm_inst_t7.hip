@@ -1,9 +1,9 @@
-// Instantiates the GEMM kernels of tile configuration 7.
+// Instantiates the GEMM kernels of tile configuration 7, rounded epilogue.
 #include "tcgemm_kernel.h"
 #include "tcgemm_launch.h"
 
 namespace tcg {
 hipError_t launch_t7(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s) {
-  return launch_tile<7>(stages, vec16, bf16, a, s);
+  return launch_tile<7, false>(stages, vec16, bf16, a, s);
 }
 }  // namespace tcg

@@ -11,7 +11,8 @@
 //               barrier (the single-stage case of the same page);
 //   STAGES = 0  unstaged: every wave loads its fragments straight from
 //               global memory, a few bytes at a time (the "Setting.stage
-//               off" case).
+//               off" case); only its output passes through LDS, on the
+//               epilogue path all kernels share.
 //
 // Copies move 16 bytes per lane (VEC16: a buffer load that writes LDS
 // directly, gfx950's asynchronous global->LDS copy) or, for operands whose
@@ -25,6 +26,11 @@
 //
 // Trip counts are the same for every lane of a workgroup, so every barrier
 // and MFMA runs in uniform control flow (page "Module Tolk.Uniform").
+//
+// Split K: with splits > 1 a workgroup folds one range of trips only and
+// stores its fp32 sums, unrounded and without the epilogue, into a
+// workspace; a reduction kernel adds the ranges in ascending order and
+// applies the epilogue.  Every path of one plan splits the same way.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,6 +38,7 @@
 
 #include <type_traits>
 
+#include "tcgemm_epilogue.h"
 #include "tcgemm_kernel_args.h"
 #include "tcgemm_tiles.h"
 
@@ -51,7 +58,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr uint32_t kOOB = 0x80000000u;  // a byte offset no resource here reaches
-constexpr int kOutF32 = 0, kOutF16 = 4, kOutBF16 = 5;
 
 // ---------------------------------------------------------------------------
 // LDS layout: row-major slot, 16-byte chunks, chunk index XOR-swizzled by a
@@ -161,9 +167,9 @@ __device__ __forceinline__ f32x16 mfma(const u32x4& src0, const u32x4& src1, con
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
 
 // ---------------------------------------------------------------------------
-// Where a workgroup works: (batch item, tile row, tile column).
+// Where a workgroup works: (K range, batch item, tile row, tile column).
 struct TilePos {
-  int64_t b, tm, tn;
+  int64_t split, b, tm, tn;
 };
 
 __device__ __forceinline__ TilePos tile_of(const KArgs& a) {
@@ -176,7 +182,10 @@ __device__ __forceinline__ TilePos tile_of(const KArgs& a) {
     if (wg < 8 * q) wg = (wg % 8) * q + wg / 8;
   }
   const int64_t per_batch = a.tiles_m * a.tiles_n;
+  const int64_t per_split = per_batch * a.batch;
   TilePos p;
+  p.split = wg / per_split;
+  wg -= p.split * per_split;
   p.b = wg / per_batch;
   const int64_t t = wg - p.b * per_batch;
   // grouped order: group_m tile rows at a time, column-major inside a group
@@ -192,79 +201,72 @@ __device__ __forceinline__ TilePos tile_of(const KArgs& a) {
 
 
 // ---------------------------------------------------------------------------
-// Epilogue helpers.
-__device__ __forceinline__ float relu_if(float v, int relu) {
-  return relu ? (v > 0.0f ? v : 0.0f) : v;  // Tile.relu: NaN and -0 give +0
-}
+// Where a workgroup's results go: C of its batch item with the epilogue, or
+// (split K) its range's fp32 partial sums with none.
+struct OutRef {
+  char* C;            // element (0, 0) of the M x N output, row pitch N
+  const float* bias;  // or null
+  int64_t M, N;
+  int dtype;          // kOutF32, kOutF16 or kOutBF16
+  int act;
+  int vec4, vec16;    // aligned 4-element / 16-byte stores allowed
+};
 
-__device__ __forceinline__ uint16_t to_out16(float v, int out_dtype) {
-  return out_dtype == kOutBF16 ? __builtin_bit_cast(uint16_t, (__bf16)v)
-                               : __builtin_bit_cast(uint16_t, (_Float16)v);
-}
-
-// Unstaged kernel: each lane stores its four consecutive columns directly.
-template <class T>
-__device__ __forceinline__ void store_direct(const KArgs& a, const f32x16 (&acc)[T::FM][T::FN], int64_t b,
-                                             int64_t m0, int64_t n0, int lane) {
-  const int64_t M = a.M, N = a.N;
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i) {
-    const int64_t m = m0 + 32 * i + (lane & 31);
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + 32 * j + 8 * g + 4 * (lane >> 5);
-        if (n >= N) continue;
-        float y[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = relu_if(acc[i][j][4 * g + q], a.relu);
-        const int64_t idx = b * a.stride_c + m * N + n;
-        const bool full = a.vec_store4 && (n + 4 <= N);
-        if (a.out_dtype == kOutF32) {
-          float* Cp = (float*)a.C + idx;
-          if (full) {
-            *(f32x4*)Cp = f32x4{y[0], y[1], y[2], y[3]};
-          } else {
-            for (int q = 0; q < 4; ++q)
-              if (n + q < N) Cp[q] = y[q];
-          }
-        } else {
-          uint16_t h[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = to_out16(y[q], a.out_dtype);
-          uint16_t* Cp = (uint16_t*)a.C + idx;
-          if (full) {
-            *(u32x2*)Cp = u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
-          } else {
-            for (int q = 0; q < 4; ++q)
-              if (n + q < N) Cp[q] = h[q];
-          }
-        }
-      }
-    }
+__device__ __forceinline__ OutRef out_ref(const KArgs& a, const TilePos& tp) {
+  OutRef o;
+  o.M = a.M;
+  o.N = a.N;
+  if (a.splits > 1) {
+    o.C = (char*)(a.ws + (tp.split * a.batch + tp.b) * a.M * a.N);
+    o.bias = nullptr;
+    o.dtype = kOutF32;
+    o.act = kActNone;
+    o.vec4 = o.vec16 = a.ws_vec;
+  } else {
+    o.C = (char*)a.C + tp.b * a.stride_c * (a.out_dtype == kOutF32 ? 4 : 2);
+    o.bias = a.bias;
+    o.dtype = a.out_dtype;
+    o.act = a.act;
+    o.vec4 = a.vec_store4;
+    o.vec16 = a.vec_store16;
   }
+  return o;
 }
 
-// Staged kernels: each wave writes a 32-row band of its outputs (EPW
-// columns, already rounded) into its own LDS region, then reads the band
-// back row by row and stores 16 bytes per lane, so each store instruction
-// writes whole row segments.
+// The output path of every kernel: each wave writes a 32-row band of its
+// results (EPW columns) into its own LDS region, then reads the band back
+// and stores 16 bytes per lane, so each store instruction writes whole row
+// segments.  The unstaged kernel shares this path: it stages no operand,
+// only its output.
+//
+// Two forms, chosen per kernel instantiation (GEN_EPI) so that each kernel
+// carries one: without a bias, with no activation or relu, the activation
+// is applied to the accumulators in place and the band holds rounded
+// outputs (the cheap, common case; also the split-K partial sums).
+// Otherwise (GEN_EPI) the band holds fp32 sums and the epilogue runs on the
+// read-back side, four values per lane at a time: applied in place, its bias
+// loads, branches and transcendental functions would be copied into each of
+// a wave's 64 groups.
+
+// Rounded band (no bias; activation none or relu), OUT the output type.
 template <class T, int OUT>
-__device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (&acc)[T::FM][T::FN], int64_t b,
-                                                  int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {
+__device__ __forceinline__ void store_rounded(const OutRef& o, const f32x16 (&acc)[T::FM][T::FN],
+                                              int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {
   constexpr int EPW = T::EPW, EPJ = EPW / 32;
-  const int64_t M = a.M, N = a.N;
+  const int64_t M = o.M, N = o.N;
   constexpr int osz = OUT == kOutF32 ? 4 : 2;
   constexpr int pitch = EPW * osz + 16;  // bytes per band row (padded against bank conflicts)
   lds_char* band = smem + w * T::EPI_WAVE_BYTES;
   constexpr int cpr = EPW * osz / 16;  // 16-byte chunks per band row
   constexpr int per_elem = 16 / osz;   // elements per chunk
+  const bool relu = o.act == kActRelu;
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
 #pragma unroll
     for (int jb = 0; jb < T::FN / EPJ; ++jb) {
+      // One band at a time: keeps the scheduler from pulling every
+      // accumulator out of the AGPRs at once.
+      __builtin_amdgcn_sched_barrier(0);
       const int row = lane & 31;
 #pragma unroll
       for (int jj = 0; jj < EPJ; ++jj) {
@@ -274,7 +276,10 @@ __device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (
           const int col = 32 * jj + 8 * g + 4 * (lane >> 5);
           float y[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) y[q] = relu_if(acc[i][j][4 * g + q], a.relu);
+          for (int q = 0; q < 4; ++q) {
+            const float v = acc[i][j][4 * g + q];
+            y[q] = relu ? (v > 0.0f ? v : 0.0f) : v;  // Tile.relu: NaN and -0 give +0
+          }
           if (osz == 4) {
             *(__attribute__((address_space(3))) f32x4*)(band + row * pitch + col * 4) = f32x4{y[0], y[1], y[2], y[3]};
           } else {
@@ -284,7 +289,8 @@ __device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (
           }
         }
       }
-      // Same-wave LDS accesses complete in order: the band is readable now.
+      // Same-wave LDS accesses complete in order: the band is readable now,
+      // and the next band's writes come after these reads.
       const int64_t mb = m0 + 32 * i;
       const int64_t nb = n0 + EPW * jb;
       constexpr int chunks = 32 * cpr;
@@ -296,8 +302,8 @@ __device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (
         const int64_t m = mb + r;
         const int64_t n = nb + (int64_t)ch * per_elem;
         if (m >= M || n >= N) continue;
-        char* dst = (char*)a.C + (b * a.stride_c + m * N + n) * osz;
-        if (a.vec_store16 && n + per_elem <= N) {
+        char* dst = o.C + (m * N + n) * osz;
+        if (o.vec16 && n + per_elem <= N) {
           *(u32x4*)dst = v;
         } else {
           const int cnt = (int)((N - n) < per_elem ? (N - n) : per_elem);
@@ -312,10 +318,97 @@ __device__ __forceinline__ void store_through_lds(const KArgs& a, const f32x16 (
   }
 }
 
+// fp32 band, epilogue on the read-back side (transcendental activations).
+template <class T>
+__device__ __forceinline__ void store_general(const OutRef& o, const f32x16 (&acc)[T::FM][T::FN],
+                                              int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {  constexpr int EPW = T::EPW, EPJ = EPW / 32;
+  const int64_t M = o.M, N = o.N;
+  constexpr int pitch = EPW * 4 + 16;  // bytes per band row (padded against bank conflicts)
+  lds_char* band = smem + w * T::EPI_WAVE_BYTES;
+  constexpr int cpr = EPW / 4;  // 16-byte chunks per band row
+  const int osz = o.dtype == kOutF32 ? 4 : 2;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+#pragma unroll
+    for (int jb = 0; jb < T::FN / EPJ; ++jb) {
+      // One band at a time: keeps the scheduler from pulling every
+      // accumulator out of the AGPRs at once.
+      __builtin_amdgcn_sched_barrier(0);
+      const int row = lane & 31;
+#pragma unroll
+      for (int jj = 0; jj < EPJ; ++jj) {
+        const int j = jb * EPJ + jj;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * jj + 8 * g + 4 * (lane >> 5);
+          *(__attribute__((address_space(3))) f32x4*)(band + row * pitch + col * 4) =
+              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+      }
+      // Same-wave LDS accesses complete in order: the band is readable now,
+      // and the next band's writes come after these reads.
+      const int64_t mb = m0 + 32 * i;
+      const int64_t nb = n0 + EPW * jb;
+      constexpr int chunks = 32 * cpr;
+#pragma unroll 2
+      for (int idx = lane; idx < chunks; idx += 64) {
+        const int r = idx / cpr;
+        const int ch = idx - r * cpr;
+        const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(band + r * pitch + ch * 16);
+        const int64_t m = mb + r;
+        const int64_t n = nb + 4 * ch;
+        if (m >= M || n >= N) continue;
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[q] = v[q];
+        epilogue4(y, o.bias, n, N, o.act);
+        char* dst = o.C + (m * N + n) * osz;
+        const bool full = o.vec4 && n + 4 <= N;
+        if (o.dtype == kOutF32) {
+          if (full) {
+            *(f32x4*)dst = f32x4{y[0], y[1], y[2], y[3]};
+          } else {
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) ((float*)dst)[q] = y[q];
+          }
+        } else {
+          uint16_t h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h[q] = to_out16(y[q], o.dtype);
+          if (full) {
+            *(u32x2*)dst = u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+          } else {
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) ((uint16_t*)dst)[q] = h[q];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class T, bool GEN_EPI>
+__device__ __forceinline__ void store_through_lds(const OutRef& o, const f32x16 (&acc)[T::FM][T::FN],
+                                                  int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {
+  if constexpr (GEN_EPI) {
+    store_general<T>(o, acc, m0, n0, lane, w, smem);
+  } else {
+    if (o.dtype == kOutF32)
+      store_rounded<T, kOutF32>(o, acc, m0, n0, lane, w, smem);
+    else if (o.dtype == kOutBF16)
+      store_rounded<T, kOutBF16>(o, acc, m0, n0, lane, w, smem);
+    else
+      store_rounded<T, kOutF16>(o, acc, m0, n0, lane, w, smem);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The kernel.
-template <int TID, int STAGES, bool VEC16, bool BF16IN>
-__global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
+// Tiles small enough in LDS for two workgroups per CU keep their registers
+// within half a SIMD's file (min_waves = 2), so that two can run.
+template <int TID, int STAGES, bool VEC16, bool BF16IN, bool GEN_EPI>
+__global__ __launch_bounds__(Tile<TID>::NT) __attribute__((amdgpu_waves_per_eu(Tile<TID>::MIN_WAVES)))
+void gemm_kernel(KArgs a) {
   using T = Tile<TID>;
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK, NW = T::NW, NT = T::NT;
   constexpr int FM = T::FM, FN = T::FN, KS = T::KS, WN = T::WN;
@@ -342,14 +435,19 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;  // Program.zeros
 
-  const int trips = a.trips;
+  // This workgroup's K range: trips [kt0, kt0 + trips) of the whole range.
+  const int kt0 = (int)tp.split * a.trips_per_split;
+  const int trips = (a.trips - kt0) < a.trips_per_split ? (a.trips - kt0) : a.trips_per_split;
+  const int64_t kbase = (int64_t)kt0 * BK;
   lds_char* smem_epi = nullptr;
   (void)smem_epi;
 
   if constexpr (STAGES == 0) {
     // ---------------- unstaged: fragments straight from global memory -----
+    __shared__ __attribute__((aligned(1024))) char epi_lds[T::EPI_BYTES];
+    smem_epi = (lds_char*)epi_lds;
     for (int t = 0; t < trips; ++t) {
-      const int64_t k0 = (int64_t)t * BK;
+      const int64_t k0 = kbase + (int64_t)t * BK;
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + row0 * K + k0, ((M - row0) * K - k0) * 2);
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + k0 * N + col0, ((K - k0) * N - col0) * 2);
 #pragma unroll
@@ -428,7 +526,7 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     const uint32_t b_off0 = (uint32_t)(b_r0 * N + b_c80) * 2u;
     // Copy chunk (trip) t with element loads (rows not 16-byte aligned).
     auto copy_elements = [&](int t, lds_char* slot) __attribute__((always_inline)) {
-      const int64_t k0 = (int64_t)t * BK;
+      const int64_t k0 = kbase + (int64_t)t * BK;
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + row0 * K + k0, ((M - row0) * K - k0) * 2);
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + k0 * N + col0, ((K - k0) * N - col0) * 2);
 #pragma unroll
@@ -475,7 +573,7 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     };
     auto copy_ctx = [&](int t) __attribute__((always_inline)) {
       CopyCtx c;
-      c.k0 = (int64_t)t * BK;
+      c.k0 = kbase + (int64_t)t * BK;
       c.ktail = c.k0 + BK > K;
       c.wa = make_rsrc_words(Ab + row0 * K + c.k0, ((M - row0) * K - c.k0) * 2);
       c.wb = make_rsrc_words(Bb + c.k0 * N + col0, ((K - c.k0) * N - col0) * 2);
@@ -764,37 +862,30 @@ __global__ __launch_bounds__(Tile<TID>::NT) void gemm_kernel(KArgs a) {
     }
   }
 
-  // ---------------- epilogue: relu, rounding, masked store ----------------
+  // ------- epilogue: bias, activation, rounding, masked store (or the -------
+  // ------- unrounded partial sums of this K range)                    -------
   // Lane l of MFMA block (i, j) holds, in registers 4g .. 4g+3, the four
   // consecutive columns 8g + 4(l/32) + 0..3 of row (l mod 32).
-  if constexpr (STAGES == 0) {
-    store_direct<T>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane);
-  } else {
-    if (a.out_dtype == kOutF32)
-      store_through_lds<T, kOutF32>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane, w, smem_epi);
-    else if (a.out_dtype == kOutBF16)
-      store_through_lds<T, kOutBF16>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane, w, smem_epi);
-    else
-      store_through_lds<T, kOutF16>(a, acc, tp.b, row0 + wm0, col0 + wn0, lane, w, smem_epi);
-  }
+  const OutRef o = out_ref(a, tp);
+  store_through_lds<T, GEN_EPI>(o, acc, row0 + wm0, col0 + wn0, lane, w, smem_epi);
 }
 
 // Launch one instantiation: returns hipGetLastError's result.
-template <int TID, int STAGES, bool VEC16, bool BF16IN>
+template <int TID, int STAGES, bool VEC16, bool BF16IN, bool GEN_EPI>
 hipError_t launch_one(const KArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_kernel<TID, STAGES, VEC16, BF16IN>), dim3((uint32_t)a.workgroups),
+  hipLaunchKernelGGL((gemm_kernel<TID, STAGES, VEC16, BF16IN, GEN_EPI>), dim3((uint32_t)a.workgroups),
                      dim3(Tile<TID>::NT), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int TID>
+template <int TID, bool GEN_EPI>
 hipError_t launch_tile(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s) {
-#define TCG_CASE(ST)                                                            \
-  if (stages == ST) {                                                           \
-    if (vec16) return bf16 ? launch_one<TID, ST, true, true>(a, s)              \
-                           : launch_one<TID, ST, true, false>(a, s);            \
-    return bf16 ? launch_one<TID, ST, false, true>(a, s)                        \
-                : launch_one<TID, ST, false, false>(a, s);                      \
+#define TCG_CASE(ST)                                                                  \
+  if (stages == ST) {                                                                 \
+    if (vec16) return bf16 ? launch_one<TID, ST, true, true, GEN_EPI>(a, s)           \
+                           : launch_one<TID, ST, true, false, GEN_EPI>(a, s);         \
+    return bf16 ? launch_one<TID, ST, false, true, GEN_EPI>(a, s)                     \
+                : launch_one<TID, ST, false, false, GEN_EPI>(a, s);                   \
   }
   TCG_CASE(0)
   TCG_CASE(1)

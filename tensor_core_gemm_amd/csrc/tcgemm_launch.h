@@ -1,5 +1,7 @@
-// Host-visible declarations of the per-tile launchers (one translation unit
-// per tile configuration instantiates the kernel template).
+// Host-visible declarations of the per-tile launchers.  Two translation
+// units per tile configuration instantiate the kernel template: launch_tN
+// with the rounded epilogue (no bias; none or relu; split-K partial sums)
+// and launch_tN_gen with the general one (bias, any activation).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,11 +11,21 @@
 namespace tcg {
 
 hipError_t launch_t1(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t1_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t2(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t2_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t3(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t3_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t4(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t4_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t5(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t5_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t6(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t6_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t7(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t7_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+
+// The split-K reduction (tcgemm_reduce.hip).
+hipError_t launch_splitk_reduce(const RArgs& r, hipStream_t s);
 
 }  // namespace tcg

@@ -17,21 +17,43 @@ struct TileDesc {
   int bm, bn, bk;
   int wm, wn;      // wave grid
   int max_stages;  // deepest LDS ring the kernel is built for
+  int min_waves;   // waves per SIMD the register budget must allow (workgroups per CU)
 };
 
 // id 0 is "planner's choice" in the ABI; real ids start at 1.
 constexpr TileDesc kTiles[] = {
-    {1, 256, 256, 64, 2, 2, 2},  // wave 128 x 128: large MFMA-bound products
-    {2, 128, 128, 64, 2, 2, 2},  // wave 64 x 64: mid sizes / more workgroups
-    {3, 64, 64, 64, 2, 2, 2},    // wave 32 x 32: small and ragged products
-    {4, 256, 96, 32, 4, 1, 2},   // wave 64 x 96: short-K, N a multiple of 96
-    {5, 128, 288, 32, 4, 1, 2},  // wave 32 x 288: short-K, N = 288 in one tile
-    {6, 256, 256, 32, 2, 2, 4},  // wave 128 x 128, half-depth slots: up to 4 in flight
-    {7, 128, 128, 32, 2, 2, 4},  // wave 64 x 64, half-depth slots: up to 4 in flight
+    {1, 256, 256, 64, 2, 2, 2, 1},  // wave 128 x 128: large MFMA-bound products
+    {2, 128, 128, 64, 2, 2, 2, 2},  // wave 64 x 64: mid sizes / more workgroups
+    {3, 64, 64, 64, 2, 2, 2, 2},    // wave 32 x 32: small and ragged products
+    {4, 256, 96, 32, 4, 1, 2, 2},   // wave 64 x 96: short-K, N a multiple of 96
+    {5, 128, 288, 32, 4, 1, 2, 1},  // wave 32 x 288: short-K, N = 288 in one tile
+    {6, 256, 256, 32, 2, 2, 4, 1},  // wave 128 x 128, half-depth slots: up to 4 in flight
+    {7, 128, 128, 32, 2, 2, 4, 2},  // wave 64 x 64, half-depth slots: up to 4 in flight
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 constexpr int kMfmaM = 32, kMfmaN = 32, kMfmaK = 16;  // v_mfma_f32_32x32x16_{bf16,f16}
+
+// Epilogue band of a configuration: 32 rows x EPW columns per wave (EPW a
+// multiple of 32 dividing the wave tile's width), fp32, rows padded by 16
+// bytes; the bands of all waves should fit in one LDS slot (else the
+// narrowest band is used and the first slot grows to hold it).
+constexpr int epi_band_width(const TileDesc& d) {
+  const int nw = d.wm * d.wn, wtn = d.bn / d.wn;
+  const int slot = (d.bm * d.bk + d.bk * d.bn) * 2;
+  int best = 32;
+  for (int e = 32; e <= wtn; e += 32)
+    if (wtn % e == 0 && nw * 32 * (e * 4 + 16) <= slot) best = e;
+  return best;
+}
+constexpr int epi_bytes(const TileDesc& d) { return d.wm * d.wn * 32 * (epi_band_width(d) * 4 + 16); }
+constexpr int slot_bytes(const TileDesc& d) { return (d.bm * d.bk + d.bk * d.bn) * 2; }
+// LDS a kernel of this configuration declares with `stages` slots (0: the
+// unstaged kernel, which holds only the epilogue bands).
+constexpr int lds_bytes_for(const TileDesc& d, int stages) {
+  return stages == 0 ? epi_bytes(d)
+                     : (slot_bytes(d) > epi_bytes(d) ? slot_bytes(d) : epi_bytes(d)) + (stages - 1) * slot_bytes(d);
+}
 
 // Compile-time view of one configuration.
 template <int ID>
@@ -39,6 +61,7 @@ struct Tile {
   static constexpr TileDesc d = kTiles[ID - 1];
   static constexpr int BM = d.bm, BN = d.bn, BK = d.bk, WM = d.wm, WN = d.wn;
   static constexpr int MAX_STAGES = d.max_stages;
+  static constexpr int MIN_WAVES = d.min_waves;
   static constexpr int NW = WM * WN;            // waves per workgroup
   static constexpr int NT = NW * 64;            // lanes per workgroup
   static constexpr int WTM = BM / WM;           // wave tile rows
@@ -55,18 +78,10 @@ struct Tile {
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BK * BN * 2;
   static constexpr int SLOT = A_BYTES + B_BYTES;
-  // Epilogue band: 32 rows x EPW columns per wave (EPW a multiple of 32
-  // dividing WTN), fp32 worst case, rows padded by 16 bytes; the bands of
-  // all waves must fit in the first LDS slot (or a little more).
-  static constexpr int epw_for(int avail) {
-    int best = 32;
-    for (int e = 32; e <= WTN; e += 32)
-      if (WTN % e == 0 && NW * 32 * (e * 4 + 16) <= avail) best = e;
-    return best;
-  }
-  static constexpr int EPW = epw_for(SLOT);
+  static constexpr int EPW = epi_band_width(d);  // epilogue band width (columns)
   static constexpr int EPI_WAVE_BYTES = 32 * (EPW * 4 + 16);
   static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
+  static_assert(EPI_BYTES == epi_bytes(d) && SLOT == slot_bytes(d), "one layout for host and device");
   static_assert(WTM % kMfmaM == 0 && WTN % kMfmaN == 0, "wave tile must be MFMA blocks");
   static_assert(BK % kMfmaK == 0 && BK % 8 == 0, "BK must be whole k-steps and chunks");
   static_assert(BN % 8 == 0, "BN must be whole chunks");

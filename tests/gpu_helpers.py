@@ -22,11 +22,13 @@ def out_torch(dtype):
 
 
 def run(tcg, A, B, w, flags=0, tile=0, guard=0, sentinel=None, plan=None, a_offset=0,
-        b_offset=0):
-    """Run C = epilogue(A.B) on the GPU; A, B are CPU tensors.  With guard > 0
-    the output sits inside a larger buffer filled with `sentinel` bits;
-    returns (C, whole buffer) on the CPU.  a_offset/b_offset shift the
-    operands by that many elements inside their device buffers."""
+        b_offset=0, bias=None, split_k=0, ws_fill=None):
+    """Run C = epilogue(A.B + bias) on the GPU; A, B (and bias) are CPU
+    tensors.  With guard > 0 the output sits inside a larger buffer filled
+    with `sentinel` bits; returns (C, whole buffer, plan) on the CPU.
+    a_offset/b_offset shift the operands by that many elements inside their
+    device buffers.  A split-K plan gets a workspace filled with ws_fill
+    (NaN by default: its contents on entry must not matter)."""
     dev = torch.device("cuda")
     Ad = torch.empty(A.numel() + a_offset, dtype=A.dtype, device=dev)
     Ad[a_offset:].copy_(A.reshape(-1))
@@ -40,15 +42,28 @@ def run(tcg, A, B, w, flags=0, tile=0, guard=0, sentinel=None, plan=None, a_offs
     else:
         buf.zero_()
     C = buf[guard:guard + n_out]
+    if bias is not None:
+        flags |= tcg.FLAG_BIAS
     if plan is None:
         plan = tcg.gemm_plan(tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
                                            flags, w.batch,
                                            w.M * w.K if w.batch > 1 else 0,
                                            w.K * w.N if w.batch > 1 else 0,
-                                           w.M * w.N if w.batch > 1 else 0, tile))
-    note(f"{w.name} M={w.M} N={w.N} K={w.K} batch={w.batch} flags={flags} tile={tile} "
-         f"plan: {plan.describe()}")
-    tcg.gemm_run(plan, Ad[a_offset:] if a_offset else Ad, Bd[b_offset:] if b_offset else Bd, C)
+                                           w.M * w.N if w.batch > 1 else 0, tile, split_k))
+    note(f"{w.name} M={w.M} N={w.N} K={w.K} batch={w.batch} epi={w.epilogue} flags={flags} "
+         f"tile={tile} split_k={split_k} plan: {plan.describe()}")
+    ws_bytes = plan.info().workspace_bytes
+    ws = None
+    if ws_bytes:
+        ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=dev)
+        ws.fill_(float("nan") if ws_fill is None else ws_fill)
+    bias_d = bias.to(dev, torch.float32).contiguous() if bias is not None else None
+    a_arg = Ad[a_offset:] if a_offset else Ad
+    b_arg = Bd[b_offset:] if b_offset else Bd
+    if bias_d is None and ws is None:
+        tcg.gemm_run(plan, a_arg, b_arg, C)
+    else:
+        tcg.gemm_run_ex(plan, a_arg, b_arg, C, bias=bias_d, workspace=ws)
     torch.cuda.synchronize()
     shape = (w.batch, w.M, w.N)
     return C.cpu().reshape(shape), buf.cpu(), plan
@@ -75,10 +90,20 @@ def rel_errors(c, y, sigma):
     return np.abs(c - y) / np.maximum(np.abs(y), 0.01 * sigma)
 
 
-def check_against_oracle(w, A, B, C):
+BOUNDED = (4, 5)  # sigmoid, tanh: outputs of size <= 1
+
+
+def floor_scale(w):
+    """The relative-error floor's scale: an output's standard deviation,
+    capped at 1 for the activations whose outputs are bounded by 1."""
+    s = w.sigma_out()
+    return min(s, 1.0) if w.epilogue in BOUNDED else s
+
+
+def check_against_oracle(w, A, B, C, bias=None):
     """Full comparison: exact for integer workloads, TOL otherwise."""
     Cref, Y = oracle.gemm(A, B, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
-                          batch=w.batch, want_y=True)
+                          batch=w.batch, want_y=True, bias=bias)
     got = as_values(C)
     if w.exact:
         want = oracle.to_float(w.out_dtype, Cref)
@@ -86,21 +111,21 @@ def check_against_oracle(w, A, B, C):
         assert bad.size == 0, f"{w.name}: {len(bad)} mismatches, first at {bad[:5].tolist()}"
         return 0.0
     assert np.all(np.isfinite(got)), f"{w.name}: non-finite output"
-    err = rel_errors(got, Y, w.sigma_out())
+    err = rel_errors(got, Y, floor_scale(w))
     worst = float(err.max()) if err.size else 0.0
     assert worst <= TOL, f"{w.name}: max rel err {worst:.3e} at {np.unravel_index(err.argmax(), err.shape)}"
     return worst
 
 
-def check_sampled(w, A, B, C, count=4096, seed=123):
+def check_sampled(w, A, B, C, count=4096, seed=123, bias=None):
     bi, ii, jj = gw.sample_indices(w.M, w.N, count, seed, w.batch)
     out, Y = oracle.gemm_sampled(A, B, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, bi, ii,
-                                 jj, batch=w.batch)
+                                 jj, batch=w.batch, bias=bias)
     got = as_values(C)[bi, ii, jj]
     if w.exact:
         assert np.array_equal(got, oracle.to_float(w.out_dtype, out))
         return 0.0
-    err = rel_errors(got, Y, w.sigma_out())
+    err = rel_errors(got, Y, floor_scale(w))
     worst = float(err.max())
     assert worst <= TOL, f"{w.name}: sampled max rel err {worst:.3e}"
     return worst

@@ -45,9 +45,10 @@ CAPS = tcg.make_caps()
 
 
 def plan(M, N, K, in_dtype=BF16, out_dtype=BF16, epi=EPI_RELU, flags=0, batch=1, tile=0,
-         caps=CAPS, **strides):
+         caps=CAPS, split_k=0, **strides):
     d = tcg.make_desc(M, N, K, in_dtype, out_dtype, epi, flags, batch,
-                      strides.get("sa", 0), strides.get("sb", 0), strides.get("sc", 0), tile)
+                      strides.get("sa", 0), strides.get("sb", 0), strides.get("sc", 0), tile,
+                      split_k)
     return tcg.gemm_plan_for_caps(d, caps)
 
 
@@ -89,7 +90,8 @@ def test_stage_fallbacks_follow_lds_budget():
     assert plan(4096, 4096, 4096, tile=1, caps=tcg.make_caps(async_copy=0)).info().stages == 1
     assert plan(4096, 4096, 4096, flags=tcg.FLAG_FORCE_STAGES_1).info().stages == 1
     p = plan(4096, 4096, 4096, flags=tcg.FLAG_UNSTAGED)
-    assert p.info().stages == 0 and p.info().lds_bytes == 0
+    # the unstaged kernel holds only its epilogue bands: 4 waves x 32 rows x (64 fp32 + 16 B)
+    assert p.info().stages == 0 and p.info().lds_bytes == 4 * 32 * (64 * 4 + 16)
 
 
 def test_short_k_token_projection_takes_wide_tile():
@@ -121,7 +123,11 @@ def test_invalid_descriptions():
         (dict(M=4, N=4, K=4, in_dtype=F32), tcg.GEMM_E_DTYPE),
         (dict(M=4, N=4, K=4, out_dtype=9), tcg.GEMM_E_DTYPE),
         (dict(M=4, N=4, K=4, epi=7), tcg.GEMM_E_ARG),
-        (dict(M=4, N=4, K=4, flags=8), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, flags=32), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, epi=6), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, epi=-1), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, split_k=-1), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, split_k=257), tcg.GEMM_E_ARG),
         (dict(M=4, N=4, K=4, tile=99), tcg.GEMM_E_ARG),
         (dict(M=4, N=4, K=4, batch=2, sa=15, sb=16, sc=16), tcg.GEMM_E_ARG),
         (dict(M=4, N=4, K=2**31), tcg.GEMM_E_SIZE),
@@ -180,3 +186,44 @@ def test_gemm_plan_without_a_device_fails_cleanly():
     with pytest.raises(tcg.GemmError) as e:
         tcg.gemm_plan(tcg.make_desc(64, 64, 64))
     assert e.value.code == tcg.GEMM_E_DEVICE
+
+
+def test_split_k_plans():
+    """K cut into ranges of whole trips: workgroups, trips per range and the
+    workspace follow; more ranges than trips are capped; an empty problem
+    keeps one range."""
+    i = plan(2048, 2048, 16384, tile=1, split_k=4).info()
+    assert (i.split_k, i.trips, i.trips_per_split) == (4, 256, 64)
+    assert i.workgroups == 64 * 4 and i.workspace_bytes == 4 * 2048 * 2048 * 4
+    assert i.mfma_per_run == 64 * 64 * 256 * 4  # splitting adds no MFMA
+    i = plan(1000, 1000, 1000, tile=3, split_k=3).info()  # 16 trips -> 6 + 6 + 4
+    assert (i.split_k, i.trips_per_split) == (3, 6)
+    i = plan(1000, 1000, 1000, tile=3, split_k=5).info()  # 16 trips -> 4 x 4: 4 ranges
+    assert (i.split_k, i.trips_per_split) == (4, 4)
+    i = plan(70, 90, 100, tile=3, split_k=8).info()
+    assert (i.trips, i.split_k) == (2, 2)
+    i = plan(0, 90, 100, tile=3, split_k=8).info()
+    assert i.split_k == 1 and i.workspace_bytes == 0
+    i = plan(70, 90, 0, tile=3, split_k=8).info()
+    assert i.split_k == 1 and i.workspace_bytes == 0
+    i = plan(64, 64, 4096, tile=3, split_k=2, batch=3, sa=64 * 4096, sb=4096 * 64, sc=64 * 64).info()
+    assert i.workgroups == 3 * 2 and i.workspace_bytes == 2 * 3 * 64 * 64 * 4
+    assert "split K 2 x 32 trips" in plan(64, 64, 4096, tile=3, split_k=2).describe()
+
+
+def test_planner_splits_only_when_allowed_and_useful():
+    # without the flag: never
+    assert plan(128, 128, 65536).info().split_k == 1
+    # with it: few output tiles and a long K are split; the square headline is not
+    assert plan(128, 128, 65536, flags=tcg.FLAG_SPLIT_K).info().split_k > 1
+    assert plan(512, 4096, 4096, flags=tcg.FLAG_SPLIT_K).info().split_k > 1
+    i = plan(2048, 2048, 16384, flags=tcg.FLAG_SPLIT_K).info()  # measured: 134 us vs 173 unsplit
+    assert (i.tile_id, i.split_k) == (1, 4)
+    assert plan(4096, 4096, 4096, flags=tcg.FLAG_SPLIT_K).info().split_k == 1
+    assert plan(256, 256, 256, flags=tcg.FLAG_SPLIT_K).info().split_k == 1
+
+
+def test_epilogue_is_named_in_the_description():
+    for epi, name in ((0, "none"), (1, "relu"), (2, "gelu"), (3, "gelu_erf"), (4, "sigmoid"), (5, "tanh")):
+        assert f"epilogue {name}" in plan(64, 64, 64, epi=epi).describe()
+    assert "epilogue bias+tanh" in plan(64, 64, 64, epi=5, flags=tcg.FLAG_BIAS).describe()
