@@ -185,12 +185,14 @@ def main():
 
 
 def kernel_source_sha() -> str:
-    """Hash of the kernel sources, so stale counter data is not reported."""
+    """Hash of the GEMM kernel's device sources (headers and kernel
+    instantiations; not the host planner, the probes or the reduction), so
+    that counter data taken from another kernel is not reported."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_core_gemm_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
-        if fn.endswith((".h", ".hip", ".cpp")):
+        if fn.endswith(".h") or (fn.startswith("tcgemm_inst_") and fn.endswith(".hip")):
             with open(os.path.join(csrc, fn), "rb") as f:
                 h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]

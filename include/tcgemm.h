@@ -83,13 +83,17 @@ enum {
  *     to gemm_run_ex).
  *   GEMM_FLAG_SPLIT_K: with split_k == 0, let the planner split K where
  *     that is estimated faster (few output tiles, long K); such a plan
- *     needs a workspace (gemm_plan_info.workspace_bytes). */
+ *     needs a workspace (gemm_plan_info.workspace_bytes).
+ *   GEMM_FLAG_TUNED: with tile == 0 and split_k == 0, take the choice an
+ *     earlier gemm_autotune measured for this problem on this device, if
+ *     any (else the planner's). */
 enum {
   GEMM_FLAG_FORCE_STAGES_1 = 1,
   GEMM_FLAG_UNSTAGED = 2,
   GEMM_FLAG_FORCE_STAGES_2 = 4,
   GEMM_FLAG_BIAS = 8,
-  GEMM_FLAG_SPLIT_K = 16
+  GEMM_FLAG_SPLIT_K = 16,
+  GEMM_FLAG_TUNED = 32
 };
 
 /* Error codes. */
@@ -213,6 +217,40 @@ int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stre
  */
 int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void* C, const gemm_run_args* args,
                 void* stream);
+
+/*
+ * Measure and keep the fastest configuration for a problem (page
+ * "gizml:tile", tune: each configuration timed on this GPU for these
+ * shapes, the fastest kept, measured once and then cached; every
+ * configuration computes the same result, exactly so wherever the sums are
+ * exact, and the run may not read what it writes).
+ *
+ * Candidates are every tile configuration (desc->tile == 0) or the one
+ * given, each unsplit and, with GEMM_FLAG_SPLIT_K, split into 2, 4, 8 or 16
+ * ranges of at least 4 trips where args->workspace holds the partial sums.
+ * Each candidate runs once to warm up, then 5 times, each timed with HIP
+ * events on `stream`; the smallest time wins.  A and B are read; C and the
+ * workspace are written many times; the bias (GEMM_FLAG_BIAS) is read.
+ * The call synchronises `stream` and returns a new plan for the winner in
+ * *out (the caller destroys it).  The choice is kept in a process-wide
+ * cache keyed by the device's architecture and CU count and by every field
+ * of desc but tile, split_k and GEMM_FLAG_TUNED; gemm_plan with
+ * GEMM_FLAG_TUNED reads it.  Errors: as gemm_plan and gemm_run_ex, and
+ * GEMM_E_LAUNCH if timing fails.
+ */
+int gemm_autotune(const gemm_desc* desc, const void* A, const void* B, void* C, const gemm_run_args* args,
+                  void* stream, gemm_plan_t* out);
+
+/* The autotune cache as text, one problem per line (device key, problem
+ * fields, chosen tile and split, measured microseconds): write it to
+ * `path`, read entries from `path` (added to or replacing those held), or
+ * forget every entry.  Return GEMM_OK, or GEMM_E_ARG if the file cannot be
+ * opened or a line does not parse. */
+int gemm_tune_cache_save(const char* path);
+int gemm_tune_cache_load(const char* path);
+void gemm_tune_cache_clear(void);
+/* Number of entries held. */
+int gemm_tune_cache_size(void);
 
 /* Free a plan (NULL is ignored). */
 void gemm_plan_destroy(gemm_plan_t plan);

@@ -12,7 +12,8 @@ import torch
 
 from .capi import (BF16, EPI_GELU, EPI_GELU_ERF, EPI_NONE, EPI_RELU, EPI_SIGMOID, EPI_TANH, F16,
                    F32, FLAG_BIAS, FLAG_FORCE_STAGES_1, FLAG_FORCE_STAGES_2, FLAG_SPLIT_K,
-                   FLAG_UNSTAGED, GEMM_E_ALIAS, GEMM_E_ALIGN, GEMM_E_ARG, GEMM_E_DEVICE,
+                   FLAG_TUNED, FLAG_UNSTAGED, gemm_autotune, gemm_tune_cache_clear,
+                   gemm_tune_cache_load, gemm_tune_cache_save, gemm_tune_cache_size, GEMM_E_ALIAS, GEMM_E_ALIGN, GEMM_E_ARG, GEMM_E_DEVICE,
                    GEMM_E_DTYPE, GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE,
                    GEMM_E_WORKSPACE, GEMM_OK, CODE_TO_TORCH, TORCH_TO_CODE, GemmError, Plan,
                    check_runtime, gemm_desc, gemm_device_caps, gemm_device_caps_query, gemm_plan,
@@ -43,9 +44,15 @@ _ACT = {None: EPI_NONE, "none": EPI_NONE, "relu": EPI_RELU, "gelu": EPI_GELU,
         "gelu_erf": EPI_GELU_ERF, "sigmoid": EPI_SIGMOID, "tanh": EPI_TANH}
 
 
+# Workspace offered to gemm_autotune for split candidates: up to 16 ranges of
+# C in fp32, at most this many bytes.
+TUNE_WORKSPACE_CAP = 1 << 30
+
+
 def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | None = None,
            bias: torch.Tensor | None = None, out_dtype=None, out: torch.Tensor | None = None,
-           flags: int = 0, tile: int = 0, split_k: int = 0, stream=None) -> torch.Tensor:
+           flags: int = 0, tile: int = 0, split_k: int = 0, tune: bool = False,
+           stream=None) -> torch.Tensor:
     """C = act(A @ B + bias) with fp32 accumulation on the MFMA units.
 
     A is [M, K] or [batch, M, K], B is [K, N] or [batch, K, N]; both fp16 or
@@ -55,6 +62,9 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
     (relu=True means act="relu").  out_dtype is torch.float32, float16 or
     bfloat16 (default: the input type).  split_k > 1 (or flags with
     FLAG_SPLIT_K) splits K; the workspace comes from torch's allocator.
+    tune=True measures the configurations (split ones too) the first time a
+    problem is seen and keeps the fastest (gemm_autotune); the run that
+    tunes writes `out` several times.
     """
     if A.dtype not in (torch.float16, torch.bfloat16) or B.dtype != A.dtype:
         raise TypeError("A and B must share one dtype, float16 or bfloat16")
@@ -90,9 +100,23 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
     elif tuple(out.shape) != shape or out.dtype != odt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
     with torch.cuda.device(A.device):
-        p = plan_for(M, N, K, TORCH_TO_CODE[A.dtype], TORCH_TO_CODE[odt], epi, flags, batch,
-                     M * K if batch > 1 else 0, K * N if batch > 1 else 0,
-                     M * N if batch > 1 else 0, tile, split_k)
+        strides = (M * K if batch > 1 else 0, K * N if batch > 1 else 0, M * N if batch > 1 else 0)
+        if tune and not tile and not split_k:
+            key = ("tuned", torch.cuda.current_device(), M, N, K, A.dtype, odt, epi, flags, batch)
+            p = _plan_cache.get(key)
+            if p is None:
+                tflags = flags | FLAG_SPLIT_K
+                wsb = min(16 * batch * M * N * 4, TUNE_WORKSPACE_CAP)
+                ws = torch.empty(wsb, dtype=torch.uint8, device=A.device)
+                p = gemm_autotune(make_desc(M, N, K, TORCH_TO_CODE[A.dtype], TORCH_TO_CODE[odt], epi,
+                                            tflags, batch, *strides),
+                                  A, B, out, bias=bias, workspace=ws, stream=stream)
+                if stream is not None and not isinstance(stream, int):
+                    ws.record_stream(stream)
+                _plan_cache[key] = p
+        else:
+            p = plan_for(M, N, K, TORCH_TO_CODE[A.dtype], TORCH_TO_CODE[odt], epi, flags, batch,
+                         *strides, tile, split_k)
         ws_bytes = p.info().workspace_bytes
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device) if ws_bytes else None
         gemm_run_ex(p, A, B, out, bias=bias, workspace=ws, stream=stream)

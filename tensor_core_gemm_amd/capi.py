@@ -16,6 +16,7 @@ from ._lib import lib
 F32, F16, BF16 = 0, 4, 5
 EPI_NONE, EPI_RELU, EPI_GELU, EPI_GELU_ERF, EPI_SIGMOID, EPI_TANH = 0, 1, 2, 3, 4, 5
 FLAG_FORCE_STAGES_1, FLAG_UNSTAGED, FLAG_FORCE_STAGES_2, FLAG_BIAS, FLAG_SPLIT_K = 1, 2, 4, 8, 16
+FLAG_TUNED = 32
 
 GEMM_OK = 0
 GEMM_E_ARG, GEMM_E_DTYPE, GEMM_E_ALIGN, GEMM_E_ALIAS = -1, -2, -3, -4
@@ -77,6 +78,12 @@ _SIGS = {
     "gemm_stage_depth": (ctypes.c_int, [ctypes.POINTER(gemm_device_caps), ctypes.c_int64,
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int]),
     "gemm_tile_count": (ctypes.c_int, []),
+    "gemm_autotune": (ctypes.c_int, [ctypes.POINTER(gemm_desc), _vp, _vp, _vp, ctypes.c_void_p, _vp,
+                                     ctypes.POINTER(_vp)]),
+    "gemm_tune_cache_save": (ctypes.c_int, [ctypes.c_char_p]),
+    "gemm_tune_cache_load": (ctypes.c_int, [ctypes.c_char_p]),
+    "gemm_tune_cache_clear": (None, []),
+    "gemm_tune_cache_size": (ctypes.c_int, []),
     "gemm_runtime_version": (ctypes.c_int, []),
 }
 _fns = {}
@@ -242,3 +249,34 @@ def check_runtime() -> None:
             if v != want:
                 raise RuntimeError(f"libtcgemm.so runs on HIP runtime {v}, torch on {want}: "
                                    "two HIP runtimes are loaded")
+
+
+def gemm_autotune(desc: gemm_desc, A, B, C, bias=None, workspace=None, workspace_bytes=None,
+                  stream=None) -> Plan:
+    """Time the candidate configurations on these buffers, keep the fastest
+    in the library's cache and return its plan (synchronises the stream)."""
+    if workspace_bytes is None:
+        workspace_bytes = 0
+        if workspace is not None and not isinstance(workspace, int):
+            workspace_bytes = workspace.numel() * workspace.element_size()
+    args = gemm_run_args(_ptr(bias), _ptr(workspace), workspace_bytes)
+    h = _vp()
+    _check(_fn("gemm_autotune")(ctypes.byref(desc), _ptr(A), _ptr(B), _ptr(C), ctypes.byref(args),
+                                _stream(stream), ctypes.byref(h)), "gemm_autotune")
+    return Plan(h.value, desc)
+
+
+def gemm_tune_cache_save(path: str) -> None:
+    _check(_fn("gemm_tune_cache_save")(path.encode()), "gemm_tune_cache_save")
+
+
+def gemm_tune_cache_load(path: str) -> None:
+    _check(_fn("gemm_tune_cache_load")(path.encode()), "gemm_tune_cache_load")
+
+
+def gemm_tune_cache_clear() -> None:
+    _fn("gemm_tune_cache_clear")()
+
+
+def gemm_tune_cache_size() -> int:
+    return _fn("gemm_tune_cache_size")()

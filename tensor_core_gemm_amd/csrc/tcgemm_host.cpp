@@ -7,8 +7,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <new>
+#include <string>
 
 #include "tcgemm.h"
 #include "tcgemm_launch.h"
@@ -70,7 +72,7 @@ int validate_desc(const gemm_desc* d) {
     return GEMM_E_DTYPE;
   if (d->epilogue < GEMM_EPI_NONE || d->epilogue > GEMM_EPI_TANH) return GEMM_E_ARG;
   if (d->flags & ~(GEMM_FLAG_FORCE_STAGES_1 | GEMM_FLAG_UNSTAGED | GEMM_FLAG_FORCE_STAGES_2 |
-                   GEMM_FLAG_BIAS | GEMM_FLAG_SPLIT_K))
+                   GEMM_FLAG_BIAS | GEMM_FLAG_SPLIT_K | GEMM_FLAG_TUNED))
     return GEMM_E_ARG;
   if (d->tile < 0 || d->tile > tcg::kNumTiles) return GEMM_E_ARG;
   if (d->split_k < 0 || d->split_k > kMaxSplits) return GEMM_E_ARG;
@@ -157,6 +159,45 @@ void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Autotune cache: problem -> measured (tile, split).  The key is the
+// device's architecture and CU count and every field of the normalised
+// description but tile, split_k and GEMM_FLAG_TUNED.
+struct TuneChoice {
+  int32_t tile;
+  int32_t split;
+  double us;
+};
+std::mutex g_tune_mu;
+std::map<std::string, TuneChoice> g_tune;
+
+std::string tune_key(const gemm_desc& d, const gemm_device_caps& caps) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s %d %lld %lld %lld %d %d %d %d %lld %lld %lld %lld", caps.arch, caps.num_cus,
+                (long long)d.M, (long long)d.N, (long long)d.K, d.in_dtype, d.out_dtype, d.epilogue,
+                d.flags & ~GEMM_FLAG_TUNED, (long long)d.batch, (long long)d.stride_a, (long long)d.stride_b,
+                (long long)d.stride_c);
+  return buf;
+}
+
+gemm_desc normalised(const gemm_desc& in) {
+  gemm_desc d = in;
+  if (d.batch == 1) {
+    d.stride_a = d.M * d.K;
+    d.stride_b = d.K * d.N;
+    d.stride_c = d.M * d.N;
+  }
+  return d;
+}
+
+bool tuned_choice(const gemm_desc& d, const gemm_device_caps& caps, TuneChoice* out) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  auto it = g_tune.find(tune_key(d, caps));
+  if (it == g_tune.end()) return false;
+  *out = it->second;
+  return true;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -236,11 +277,11 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
   int rc = validate_desc(desc);
   if (rc) return rc;
   if (!caps || caps->num_cus <= 0 || caps->wave_size != 64) return GEMM_E_DEVICE;
-  gemm_desc d = *desc;
-  if (d.batch == 1) {
-    d.stride_a = d.M * d.K;
-    d.stride_b = d.K * d.N;
-    d.stride_c = d.M * d.N;
+  gemm_desc d = normalised(*desc);
+  TuneChoice tc;
+  if ((d.flags & GEMM_FLAG_TUNED) && d.tile == 0 && d.split_k == 0 && tuned_choice(d, *caps, &tc)) {
+    d.tile = tc.tile;
+    d.split_k = tc.split;
   }
   int id = 0;
   int64_t want_splits = 1;
@@ -492,4 +533,139 @@ extern "C" int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void*
     return GEMM_E_LAUNCH;
   }
   return GEMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Autotune (page "gizml:tile", tune).
+extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B, void* C,
+                             const gemm_run_args* args, void* stream, gemm_plan_t* out) {
+  if (!out) return GEMM_E_ARG;
+  *out = nullptr;
+  int rc = validate_desc(desc);
+  if (rc) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_E_DEVICE;
+  }
+  gemm_device_caps caps;
+  rc = cached_caps(dev, &caps);
+  if (rc) return rc;
+  const gemm_desc base = normalised(*desc);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    (void)hipGetLastError();
+    return GEMM_E_LAUNCH;
+  }
+  const int64_t ws_have = (args && args->workspace) ? args->workspace_bytes : 0;
+  const int lo = base.tile ? base.tile : 1, hi = base.tile ? base.tile : tcg::kNumTiles;
+  TuneChoice best{0, 1, 1e300};
+  rc = GEMM_OK;
+  for (int id = lo; id <= hi && rc == GEMM_OK; ++id) {
+    int last_split = 0;
+    for (int sp = 1; sp <= 16; sp *= 2) {
+      if (sp > 1 && !(base.flags & GEMM_FLAG_SPLIT_K)) break;
+      gemm_desc d = base;
+      d.tile = id;
+      d.split_k = sp;
+      d.flags &= ~GEMM_FLAG_TUNED;
+      gemm_plan_t h = nullptr;
+      if (gemm_plan_for_caps(&d, &caps, &h) != GEMM_OK) continue;
+      const gemm_plan_info& in = reinterpret_cast<Plan*>(h)->info;
+      const bool usable = in.split_k == sp && in.split_k != last_split && in.workspace_bytes <= ws_have &&
+                          (sp == 1 || in.trips_per_split >= 4);
+      if (!usable) {
+        gemm_plan_destroy(h);
+        continue;
+      }
+      last_split = in.split_k;
+      double t_min = 1e300;
+      int r = gemm_run_ex(h, A, B, C, args, stream);  // warm-up
+      for (int rep = 0; rep < 5 && r == GEMM_OK; ++rep) {
+        float ms = 0.0f;
+        if (hipEventRecord(e0, s) != hipSuccess || (r = gemm_run_ex(h, A, B, C, args, stream)) != GEMM_OK ||
+            hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+            hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+          if (r == GEMM_OK) r = GEMM_E_LAUNCH;
+          break;
+        }
+        t_min = std::min(t_min, 1e3 * (double)ms);
+      }
+      gemm_plan_destroy(h);
+      if (r != GEMM_OK) {
+        rc = r;
+        break;
+      }
+      if (log_enabled())
+        std::fprintf(stderr, "[tcgemm] tune %lldx%lldx%lld: tile %d split %d: %.2f us\n", (long long)d.M,
+                     (long long)d.N, (long long)d.K, id, sp, t_min);
+      if (t_min < best.us) best = TuneChoice{id, sp, t_min};
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  (void)hipGetLastError();
+  if (rc != GEMM_OK) return rc;
+  if (best.tile == 0) return GEMM_E_PLAN;  // no candidate could run
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tune[tune_key(base, caps)] = best;
+  }
+  gemm_desc d = base;
+  d.tile = best.tile;
+  d.split_k = best.split;
+  d.flags &= ~GEMM_FLAG_TUNED;
+  return gemm_plan_for_caps(&d, &caps, out);
+}
+
+extern "C" int gemm_tune_cache_save(const char* path) {
+  if (!path) return GEMM_E_ARG;
+  FILE* f = std::fopen(path, "w");
+  if (!f) return GEMM_E_ARG;
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  for (const auto& kv : g_tune)
+    std::fprintf(f, "%s %d %d %.3f\n", kv.first.c_str(), kv.second.tile, kv.second.split, kv.second.us);
+  return std::fclose(f) == 0 ? GEMM_OK : GEMM_E_ARG;
+}
+
+extern "C" int gemm_tune_cache_load(const char* path) {
+  if (!path) return GEMM_E_ARG;
+  FILE* f = std::fopen(path, "r");
+  if (!f) return GEMM_E_ARG;
+  char line[512];
+  int rc = GEMM_OK;
+  std::map<std::string, TuneChoice> read;
+  while (std::fgets(line, sizeof(line), f)) {
+    char arch[64];
+    int cus, in, o, epi, flags, tile, split;
+    long long M, N, K, batch, sa, sb, sc;
+    double us;
+    if (std::sscanf(line, "%63s %d %lld %lld %lld %d %d %d %d %lld %lld %lld %lld %d %d %lf", arch, &cus, &M, &N,
+                    &K, &in, &o, &epi, &flags, &batch, &sa, &sb, &sc, &tile, &split, &us) != 16 ||
+        tile < 1 || tile > tcg::kNumTiles || split < 1 || split > kMaxSplits) {
+      rc = GEMM_E_ARG;
+      break;
+    }
+    char key[256];
+    std::snprintf(key, sizeof(key), "%s %d %lld %lld %lld %d %d %d %d %lld %lld %lld %lld", arch, cus, M, N, K, in,
+                  o, epi, flags, batch, sa, sb, sc);
+    read[key] = TuneChoice{tile, split, us};
+  }
+  std::fclose(f);
+  if (rc != GEMM_OK) return rc;
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  for (const auto& kv : read) g_tune[kv.first] = kv.second;
+  return GEMM_OK;
+}
+
+extern "C" void gemm_tune_cache_clear(void) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tune.clear();
+}
+
+extern "C" int gemm_tune_cache_size(void) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  return (int)g_tune.size();
 }

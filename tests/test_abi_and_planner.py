@@ -123,7 +123,7 @@ def test_invalid_descriptions():
         (dict(M=4, N=4, K=4, in_dtype=F32), tcg.GEMM_E_DTYPE),
         (dict(M=4, N=4, K=4, out_dtype=9), tcg.GEMM_E_DTYPE),
         (dict(M=4, N=4, K=4, epi=7), tcg.GEMM_E_ARG),
-        (dict(M=4, N=4, K=4, flags=32), tcg.GEMM_E_ARG),
+        (dict(M=4, N=4, K=4, flags=64), tcg.GEMM_E_ARG),
         (dict(M=4, N=4, K=4, epi=6), tcg.GEMM_E_ARG),
         (dict(M=4, N=4, K=4, epi=-1), tcg.GEMM_E_ARG),
         (dict(M=4, N=4, K=4, split_k=-1), tcg.GEMM_E_ARG),
@@ -227,3 +227,39 @@ def test_epilogue_is_named_in_the_description():
     for epi, name in ((0, "none"), (1, "relu"), (2, "gelu"), (3, "gelu_erf"), (4, "sigmoid"), (5, "tanh")):
         assert f"epilogue {name}" in plan(64, 64, 64, epi=epi).describe()
     assert "epilogue bias+tanh" in plan(64, 64, 64, epi=5, flags=tcg.FLAG_BIAS).describe()
+
+
+def test_tune_cache_file_round_trip_and_tuned_plans(tmp_path):
+    """A cache line names the device, the problem and the measured choice;
+    gemm_plan with GEMM_FLAG_TUNED takes it, other problems keep the
+    planner's choice, and a malformed file is refused."""
+    tcg.gemm_tune_cache_clear()
+    assert tcg.gemm_tune_cache_size() == 0
+    arch = CAPS.arch.decode()
+    M, N, K = 1000, 1000, 1000
+    line = f"{arch} 256 {M} {N} {K} {BF16} {BF16} {EPI_RELU} {tcg.FLAG_SPLIT_K} 1 {M*K} {K*N} {M*N} 2 2 12.5\n"
+    f = tmp_path / "tune.txt"
+    f.write_text(line)
+    tcg.gemm_tune_cache_load(str(f))
+    assert tcg.gemm_tune_cache_size() == 1
+    i = plan(M, N, K, flags=tcg.FLAG_SPLIT_K | tcg.FLAG_TUNED).info()
+    assert (i.tile_id, i.split_k) == (2, 2)
+    # the same problem without the flag, or another problem: the planner's choice
+    assert plan(M, N, K, flags=tcg.FLAG_SPLIT_K).info().tile_id == 3
+    assert plan(M, N, K + 8, flags=tcg.FLAG_SPLIT_K | tcg.FLAG_TUNED).info().tile_id == 3
+    # a tile or split given explicitly wins over the cache
+    assert plan(M, N, K, flags=tcg.FLAG_SPLIT_K | tcg.FLAG_TUNED, tile=1).info().tile_id == 1
+    g = tmp_path / "saved.txt"
+    tcg.gemm_tune_cache_save(str(g))
+    assert g.read_text().split()[:13] == line.split()[:13]
+    tcg.gemm_tune_cache_clear()
+    tcg.gemm_tune_cache_load(str(g))
+    assert plan(M, N, K, flags=tcg.FLAG_SPLIT_K | tcg.FLAG_TUNED).info().split_k == 2
+    bad = tmp_path / "bad.txt"
+    bad.write_text("gfx950 256 1 2 3\n")
+    with pytest.raises(tcg.GemmError) as e:
+        tcg.gemm_tune_cache_load(str(bad))
+    assert e.value.code == tcg.GEMM_E_ARG
+    with pytest.raises(tcg.GemmError):
+        tcg.gemm_tune_cache_load(str(tmp_path / "missing.txt"))
+    tcg.gemm_tune_cache_clear()

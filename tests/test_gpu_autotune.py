@@ -1,0 +1,83 @@
+"""The autotuner on the GPU (page "gizml:tile", tune: each configuration
+timed on this GPU for these shapes, the fastest kept and cached; every
+configuration must compute the same result)."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_workloads as gw
+import oracle
+from gemm_workloads import BF16, EPI_NONE, EPI_RELU, F16, F32
+from gpu_helpers import as_bits, check_against_oracle, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tcg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_core_gemm_amd as t
+    t.check_runtime()
+    return t
+
+
+def test_every_candidate_gives_the_same_bits_on_integers(tcg):
+    """Integer operands with sums below 2^24: every tile and every split
+    computes the one exact result."""
+    M, N, K = 300, 200, 1024
+    w = gw.custom(M, N, K, F16, F32, EPI_RELU, gw.INT4, seed=90)
+    A, B = gw.make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    want = oracle.gemm(A, B, M, N, K, F16, F32, EPI_RELU).reshape(M, N)
+    ws = torch.empty(16 * M * N, dtype=torch.float32, device="cuda")
+    for tile in range(1, tcg.gemm_tile_count() + 1):
+        for split in (1, 2, 4, 8, 16):
+            p = tcg.gemm_plan(tcg.make_desc(M, N, K, F16, F32, EPI_RELU, 0, tile=tile, split_k=split))
+            C = torch.full((M, N), float("nan"), device="cuda")
+            note(f"tile {tile} split {split}: {p.describe()}")
+            tcg.gemm_run_ex(p, Ad, Bd, C, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(C.cpu().numpy(), want), (tile, split)
+
+
+def test_autotune_picks_caches_and_replays(tcg):
+    tcg.gemm_tune_cache_clear()
+    M, N, K = 256, 512, 8192  # few tiles, long K: splits are candidates
+    w = gw.custom(M, N, K, BF16, F32, EPI_NONE, gw.INT4, seed=91)
+    A, B = gw.make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(16 * M * N, dtype=torch.float32, device="cuda")
+    desc = tcg.make_desc(M, N, K, BF16, F32, EPI_NONE, tcg.FLAG_SPLIT_K)
+    note("autotune 256x512x8192")
+    p = tcg.gemm_autotune(desc, Ad, Bd, C, workspace=ws)
+    note(f"chosen: {p.describe()}")
+    assert tcg.gemm_tune_cache_size() == 1
+    # the tuned plan computes the exact result
+    C.fill_(float("nan"))
+    tcg.gemm_run_ex(p, Ad, Bd, C, workspace=ws)
+    torch.cuda.synchronize()
+    check_against_oracle(w, A, B, C.cpu().reshape(1, M, N))
+    # gemm_plan with GEMM_FLAG_TUNED returns the same choice
+    q = tcg.gemm_plan(tcg.make_desc(M, N, K, BF16, F32, EPI_NONE, tcg.FLAG_SPLIT_K | tcg.FLAG_TUNED))
+    assert (q.info().tile_id, q.info().split_k) == (p.info().tile_id, p.info().split_k)
+    # without a workspace no split is a candidate
+    tcg.gemm_tune_cache_clear()
+    p1 = tcg.gemm_autotune(desc, Ad, Bd, C)
+    assert p1.info().split_k == 1
+    tcg.gemm_tune_cache_clear()
+
+
+def test_matmul_tune_within_tolerance(tcg):
+    tcg.gemm_tune_cache_clear()
+    w = gw.custom(512, 1024, 2048, BF16, BF16, EPI_RELU, gw.NORMAL, seed=92)
+    A, B = gw.make_inputs(w)
+    note("matmul tune=True 512x1024x2048")
+    C = tcg.matmul(A.cuda(), B.cuda(), relu=True, tune=True)
+    C2 = tcg.matmul(A.cuda(), B.cuda(), relu=True, tune=True)  # cached plan: same bits
+    torch.cuda.synchronize()
+    assert tcg.gemm_tune_cache_size() == 1
+    assert np.array_equal(as_bits(C.cpu()), as_bits(C2.cpu()))
+    check_against_oracle(w, A, B, C.cpu().reshape(1, w.M, w.N))
+    tcg.gemm_tune_cache_clear()
