@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of C = epilogue(A . B) on one MI355X: prints one JSON line.
 
-A step is one gemm_run of the workload over inputs already resident in HBM.
+A step is one gemm_run of the workload over inputs already resident in HBM
+(the planner's plan, split K allowed: a split plan's step is the GEMM and
+its reduction).
 Default workload: bf16 M = N = K = 4096, A, B ~ N(0, 1), relu, bf16 out
 (the headline GEMM).  W untimed warm-up steps, then K timed steps between
 two device synchronisations; the average launch duration of the kernel is
@@ -40,6 +42,7 @@ def parse():
     ap.add_argument("--workload", default="bf16_4096_relu")
     ap.add_argument("--tile", type=int, default=0, help="force a tile configuration id")
     ap.add_argument("--flags", type=int, default=0, help="plan flags (1: one stage, 2: unstaged)")
+    ap.add_argument("--no-split", action="store_true", help="do not let the planner split K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -90,15 +93,21 @@ def main():
         B = B_cpu.to(dev) if r == 0 else B_cpu.to(dev).clone()
         C = torch.empty((w.M, w.N), dtype=gw.TORCH_DTYPE[w.out_dtype], device=dev)
         sets.append((A, B, C))
-    desc = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, args.flags,
+    flags = args.flags | (0 if args.no_split else tcg.FLAG_SPLIT_K)
+    desc = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, flags,
                          tile=args.tile)
     plan = tcg.gemm_plan(desc)
     info = plan.info()
     stream = torch.cuda.current_stream()
+    ws = (torch.empty(info.workspace_bytes, dtype=torch.uint8, device=dev)
+          if info.workspace_bytes else None)
 
     def step(i):
         A, B, C = sets[i % len(sets)]
-        tcg.gemm_run(plan, A, B, C, stream)
+        if ws is None:
+            tcg.gemm_run(plan, A, B, C, stream)
+        else:
+            tcg.gemm_run_ex(plan, A, B, C, workspace=ws, stream=stream)
 
     for i in range(args.warmup):
         step(i)
