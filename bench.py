@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the GEMM, run a plain device copy of this many MiB three "
                          "times (a known-size reference for the HBM byte counters)")
+    ap.add_argument("--vs-torch", action="store_true",
+                    help="also time torch.matmul (the vendor BLAS) on the same resident inputs, "
+                         "the same way, with the activation as a separate op; reported as context")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -188,9 +191,41 @@ def main():
             "algorithmic_bytes_per_launch": w.algorithmic_bytes,
         },
     }
+    if args.vs_torch:
+        result["torch_matmul"] = torch_matmul_time(w, sets[0], args.warmup, K, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, A_cpu, B_cpu, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def torch_matmul_time(w, io, warmup, steps, stream):
+    """torch.matmul (the vendor BLAS on ROCm) on the same resident inputs,
+    timed like the steps above; relu, where the workload has it, is a
+    separate in-place op."""
+    import torch
+    A, B, C = io
+    A2, B2 = A.view(w.M, w.K), B.view(w.K, w.N)
+    same_type = C.dtype == A.dtype
+
+    def step():
+        if same_type:
+            torch.matmul(A2, B2, out=C)
+            y = C
+        else:
+            y = torch.matmul(A2, B2).to(C.dtype)
+        if w.epilogue:
+            torch.relu_(y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms_per_step": round(ms, 5), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2),
+            "with_relu": bool(w.epilogue)}
 
 
 def kernel_source_sha() -> str:
