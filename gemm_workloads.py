@@ -7,7 +7,8 @@ fp16/bf16 by torch's ``.to``) and lists the workloads.  Both sides consume
 the same 16-bit tensors, so input rounding is not part of any comparison.
 
 Storage codes are those of the page "gizml:tile" (Constants): F32 = 0,
-F16 = 4, BF16 = 5.
+F16 = 4, BF16 = 5, FP8 = 9 (E4M3 operands: torch's float8_e4m3fn, the OCP
+format).
 
 The five workloads:
 
@@ -33,11 +34,12 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-F32, F16, BF16 = 0, 4, 5
+F32, F16, BF16, FP8 = 0, 4, 5, 9
 EPI_NONE, EPI_RELU, EPI_GELU, EPI_GELU_ERF, EPI_SIGMOID, EPI_TANH = 0, 1, 2, 3, 4, 5
 
-TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
-DTYPE_NAME = {F32: "f32", F16: "f16", BF16: "bf16"}
+TORCH_DTYPE = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16,
+               FP8: torch.float8_e4m3fn}
+DTYPE_NAME = {F32: "f32", F16: "f16", BF16: "bf16", FP8: "fp8e4m3"}
 
 
 @dataclass(frozen=True)

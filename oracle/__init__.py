@@ -16,7 +16,7 @@ bias row added in F32 (Tile.add, broadcast over rows), an activation
 Tile.sigmoid, Tile.tanh; the transcendental ones from their definitions in
 double precision, rounded once to F32), then rounding to the storage type
 (Tile.to).  Storage codes are the page's constants: F32 = 0, F16 = 4,
-BF16 = 5.
+BF16 = 5, FP8 = 9 (operands only; E4M3, read as the OCP format).
 """
 from __future__ import annotations
 
@@ -27,7 +27,7 @@ import threading
 
 import numpy as np
 
-F32, F16, BF16 = 0, 4, 5
+F32, F16, BF16, FP8 = 0, 4, 5, 9
 EPI_NONE, EPI_RELU, EPI_GELU, EPI_GELU_ERF, EPI_SIGMOID, EPI_TANH = 0, 1, 2, 3, 4, 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,21 +83,25 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(_vp)
 
 
-def _bits(x) -> np.ndarray:
-    """Raw 16-bit patterns as a C-contiguous uint16 numpy array."""
-    if hasattr(x, "detach"):  # a torch tensor of dtype float16/bfloat16/int16
+def _bits(x, dtype: int | None = None) -> np.ndarray:
+    """Raw patterns as a C-contiguous numpy array: uint16 for F16/BF16,
+    uint8 for FP8 (dtype None: whatever width x has, 16 or 8 bits)."""
+    if hasattr(x, "detach"):  # a torch tensor of a 16- or 8-bit type
         import torch  # local: the oracle itself needs no torch
 
         t = x.detach().cpu().contiguous()
         if t.dtype in (torch.float16, torch.bfloat16):
             t = t.view(torch.int16)
+        elif t.element_size() == 1:
+            t = t.view(torch.uint8)
         x = t.numpy()
     a = np.ascontiguousarray(x)
-    if a.dtype != np.uint16:
-        a = a.view(np.uint16) if a.dtype.itemsize == 2 else None
-    if a is None:
-        raise TypeError("expected 16-bit patterns")
-    return a
+    width = None if dtype is None else (1 if dtype == FP8 else 2)
+    if a.dtype.itemsize == 2 and width in (None, 2):
+        return a.view(np.uint16)
+    if a.dtype.itemsize == 1 and width in (None, 1):
+        return a.view(np.uint8)
+    raise TypeError("expected 16-bit patterns (F16, BF16) or bytes (FP8)")
 
 
 def threads() -> int:
@@ -105,7 +109,7 @@ def threads() -> int:
 
 
 def decode(dtype: int, bits) -> np.ndarray:
-    b = _bits(bits)
+    b = _bits(bits, dtype)
     out = np.empty(b.shape, np.float32)
     _load().oracle_decode(dtype, _ptr(b), _ptr(out), b.size)
     return out
@@ -144,7 +148,7 @@ def gemm(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, epilogue: 
     Returns C as float32 (out F32) or uint16 patterns (F16/BF16), shape
     [batch, M, N], and, if ``want_y``, the fp32 value before rounding too.
     """
-    a, b = _bits(A).reshape(-1), _bits(B).reshape(-1)
+    a, b = _bits(A, in_dtype).reshape(-1), _bits(B, in_dtype).reshape(-1)
     sa = M * K if stride_a is None else stride_a
     sb = K * N if stride_b is None else stride_b
     if batch < 1 or a.size < (batch - 1) * sa + M * K or b.size < (batch - 1) * sb + K * N:
@@ -165,7 +169,7 @@ def gemm_sampled(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, ep
 
     Returns (values in out_dtype storage, fp32 y before rounding).
     """
-    a, b = _bits(A).reshape(-1), _bits(B).reshape(-1)
+    a, b = _bits(A, in_dtype).reshape(-1), _bits(B, in_dtype).reshape(-1)
     sa = M * K if stride_a is None else stride_a
     sb = K * N if stride_b is None else stride_b
     bi = np.ascontiguousarray(bi, np.int64)
@@ -187,7 +191,7 @@ def gemm_sampled(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, ep
 def gemm_f64(A, B, M: int, N: int, K: int, in_dtype: int, batch: int = 1,
              stride_a: int | None = None, stride_b: int | None = None, n_threads: int = 0):
     """fp64 twin: (sum in double before any epilogue, sum of |a||b|)."""
-    a, b = _bits(A).reshape(-1), _bits(B).reshape(-1)
+    a, b = _bits(A, in_dtype).reshape(-1), _bits(B, in_dtype).reshape(-1)
     sa = M * K if stride_a is None else stride_a
     sb = K * N if stride_b is None else stride_b
     if a.size < (batch - 1) * sa + M * K or b.size < (batch - 1) * sb + K * N:

@@ -40,12 +40,16 @@
  *   - relu(x) is x when x > 0, else +0: -0 and NaN both give +0, because
  *     max(x, 0) "with a NaN, the other value" is 0 (Tile.maximum);
  *   - K = 0 leaves the zero accumulator: C = epilogue(+0) everywhere;
- *   - the product of two fp16 (or two bf16) values is exact in fp32 except
- *     when it over- or underflows fp32's range, so FMA contraction would be
- *     immaterial; the file is still built with -ffp-contract=off so that the
- *     loop is literally fl32(acc + fl32(a*b)).
+ *   - the product of two fp16 (or two bf16, or two FP8) values is exact in
+ *     fp32 except when it over- or underflows fp32's range, so FMA
+ *     contraction would be immaterial; the file is still built with
+ *     -ffp-contract=off so that the loop is literally fl32(acc + fl32(a*b));
+ *   - the page's FP8 storage type is "FP8 E4M3" with no further detail; it
+ *     is read as the OCP 8-bit E4M3 format (bias 7, no infinities, NaN only
+ *     at S.1111.111, largest finite 448).
  *
- * Storage codes follow the page's constants (F32 = 0, F16 = 4, BF16 = 5).
+ * Storage codes follow the page's constants (F32 = 0, F16 = 4, BF16 = 5,
+ * FP8 = 9 for FP8 E4M3 operands).
  *
  * The loop order is i, k, j: every C[b,i,j] still sums k in ascending order,
  * one element per accumulator; the j loop only walks a row of outputs at a
@@ -62,6 +66,7 @@
 #define ORC_F32 0
 #define ORC_F16 4
 #define ORC_BF16 5
+#define ORC_FP8 9
 
 #define ORC_OK 0
 #define ORC_EARG (-1)
@@ -96,6 +101,32 @@ static float orc_bf16_decode(uint16_t h) {
   float v;
   memcpy(&v, &u, 4);
   return v;
+}
+
+/* FP8 E4M3 (the page's FP8 storage type; read as the OCP 8-bit E4M3 format):
+ * 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; exponent 0 holds
+ * zero and the subnormals f * 2^-9; there are no infinities, and the one
+ * pattern with all exponent and fraction bits set (0x7f, 0xff) is NaN. */
+static float orc_fp8_decode(uint8_t h) {
+  int sign = (h >> 7) & 1;
+  int e = (h >> 3) & 15;
+  int f = h & 7;
+  float v;
+  if (e == 15 && f == 7) {
+    v = NAN;
+  } else if (e == 0) {
+    v = ldexpf((float)f, -9);
+  } else {
+    v = ldexpf((float)(8 + f), e - 10); /* (1.f) * 2^(e-7) */
+  }
+  return sign ? -v : v;
+}
+
+/* Element idx of an operand array of storage type dtype. */
+static float orc_decode_at(int dtype, const void* base, int64_t idx) {
+  if (dtype == ORC_FP8) return orc_fp8_decode(((const uint8_t*)base)[idx]);
+  const uint16_t h = ((const uint16_t*)base)[idx];
+  return (dtype == ORC_F16) ? orc_f16_decode(h) : orc_bf16_decode(h);
 }
 
 /* Round an unsigned magnitude right by `shift` bits, to nearest, ties to even. */
@@ -149,10 +180,10 @@ static uint16_t orc_bf16_encode(float x) {
   return (uint16_t)hi;
 }
 
-/* Exported element-wise conversions (used by the tests that pin them). */
-void oracle_decode(int dtype, const uint16_t* src, float* dst, int64_t n) {
-  for (int64_t i = 0; i < n; ++i)
-    dst[i] = (dtype == ORC_F16) ? orc_f16_decode(src[i]) : orc_bf16_decode(src[i]);
+/* Exported element-wise conversions (used by the tests that pin them).
+ * src holds n elements of dtype (F16, BF16: 16-bit patterns; FP8: bytes). */
+void oracle_decode(int dtype, const void* src, float* dst, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = orc_decode_at(dtype, src, i);
 }
 
 void oracle_encode(int dtype, const float* src, uint16_t* dst, int64_t n) {
@@ -165,7 +196,7 @@ static int orc_check(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
                      int64_t batch) {
   if (M < 0 || N < 0 || K < 0 || batch < 1) return ORC_EARG;
   if (epilogue < 0 || epilogue > 5) return ORC_EARG;
-  if (in_dtype != ORC_F16 && in_dtype != ORC_BF16) return ORC_EDTYPE;
+  if (in_dtype != ORC_F16 && in_dtype != ORC_BF16 && in_dtype != ORC_FP8) return ORC_EDTYPE;
   if (out_dtype != ORC_F32 && out_dtype != ORC_F16 && out_dtype != ORC_BF16) return ORC_EDTYPE;
   return ORC_OK;
 }
@@ -200,6 +231,11 @@ static void orc_store(int out_dtype, void* C, int64_t idx, float y) {
     ((uint16_t*)C)[idx] = orc_bf16_encode(y);
 }
 
+/* Decode n elements starting at element `first` of an operand array. */
+static void orc_decode_batch(int dtype, const void* base, int64_t first, float* dst, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = orc_decode_at(dtype, base, first + i);
+}
+
 static void orc_set_threads(int threads) {
 #ifdef _OPENMP
   if (threads > 0) omp_set_num_threads(threads);
@@ -224,8 +260,8 @@ int oracle_max_threads(void) {
  * conversion, as a contiguous [batch][M][N] array.
  */
 int oracle_gemm(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int epilogue,
-                const float* bias, int64_t batch, const uint16_t* A, int64_t stride_a,
-                const uint16_t* B, int64_t stride_b, void* C, int64_t stride_c, float* Y,
+                const float* bias, int64_t batch, const void* A, int64_t stride_a,
+                const void* B, int64_t stride_b, void* C, int64_t stride_c, float* Y,
                 int threads) {
   int rc = orc_check(M, N, K, in_dtype, out_dtype, epilogue, batch);
   if (rc) return rc;
@@ -235,8 +271,8 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, in
   float* af = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? M * K : 1));
   if (!bf || !af) { free(bf); free(af); return ORC_ENOMEM; }
   for (int64_t b = 0; b < batch; ++b) {
-    oracle_decode(in_dtype, A + b * stride_a, af, M * K);
-    oracle_decode(in_dtype, B + b * stride_b, bf, K * N);
+    orc_decode_batch(in_dtype, A, b * stride_a, af, M * K);
+    orc_decode_batch(in_dtype, B, b * stride_b, bf, K * N);
     int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
     for (i = 0; i < M; ++i) {
@@ -267,9 +303,9 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, in
  * and, when Y is not NULL, its fp32 y to Y[e].  Same sum order as above.
  */
 int oracle_gemm_sampled(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
-                        int epilogue, const float* bias, int64_t batch, const uint16_t* A,
+                        int epilogue, const float* bias, int64_t batch, const void* A,
                         int64_t stride_a,
-                        const uint16_t* B, int64_t stride_b, int64_t count, const int64_t* bi,
+                        const void* B, int64_t stride_b, int64_t count, const int64_t* bi,
                         const int64_t* ii, const int64_t* jj, void* out, float* Y, int threads) {
   int rc = orc_check(M, N, K, in_dtype, out_dtype, epilogue, batch);
   if (rc) return rc;
@@ -280,12 +316,12 @@ int oracle_gemm_sampled(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
   int64_t e;
 #pragma omp parallel for schedule(static)
   for (e = 0; e < count; ++e) {
-    const uint16_t* arow = A + bi[e] * stride_a + ii[e] * K;
-    const uint16_t* bcol = B + bi[e] * stride_b + jj[e];
+    const int64_t arow = bi[e] * stride_a + ii[e] * K;
+    const int64_t bcol = bi[e] * stride_b + jj[e];
     float acc = 0.0f;
     for (int64_t k = 0; k < K; ++k) {
-      float a = (in_dtype == ORC_F16) ? orc_f16_decode(arow[k]) : orc_bf16_decode(arow[k]);
-      float bv = (in_dtype == ORC_F16) ? orc_f16_decode(bcol[k * N]) : orc_bf16_decode(bcol[k * N]);
+      float a = orc_decode_at(in_dtype, A, arow + k);
+      float bv = orc_decode_at(in_dtype, B, bcol + k * N);
       acc = acc + a * bv;
     }
     float y = orc_epilogue(acc, bias, jj[e], epilogue);
@@ -302,7 +338,7 @@ int oracle_gemm_sampled(int64_t M, int64_t N, int64_t K, int in_dtype, int out_d
  * Either output may be NULL.  Contiguous [batch][M][N] outputs.
  */
 int oracle_gemm_f64(int64_t M, int64_t N, int64_t K, int in_dtype, int64_t batch,
-                    const uint16_t* A, int64_t stride_a, const uint16_t* B, int64_t stride_b,
+                    const void* A, int64_t stride_a, const void* B, int64_t stride_b,
                     double* Y64, double* S64, int threads) {
   int rc = orc_check(M, N, K, in_dtype, ORC_F32, 0, batch);
   if (rc) return rc;
@@ -312,8 +348,8 @@ int oracle_gemm_f64(int64_t M, int64_t N, int64_t K, int in_dtype, int64_t batch
   float* af = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? M * K : 1));
   if (!bf || !af) { free(bf); free(af); return ORC_ENOMEM; }
   for (int64_t b = 0; b < batch; ++b) {
-    oracle_decode(in_dtype, A + b * stride_a, af, M * K);
-    oracle_decode(in_dtype, B + b * stride_b, bf, K * N);
+    orc_decode_batch(in_dtype, A, b * stride_a, af, M * K);
+    orc_decode_batch(in_dtype, B, b * stride_b, bf, K * N);
     int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
     for (i = 0; i < M; ++i) {
