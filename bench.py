@@ -29,7 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_MFMA_TFLOPS = {4: 2516.6, 5: 2516.6}  # dense fp16 / bf16, MI355X
+# MI355X dense MFMA peaks: fp16 / bf16 2516.6 TFLOP/s (256 CUs x 2.4 GHz x
+# 4096 flop/CU/clk), FP8 5033.2 (8192 flop/CU/clk)
+PEAK_MFMA_TFLOPS = {4: 2516.6, 5: 2516.6, 9: 5033.2}
 PEAK_HBM_GBS = 8000.0
 METRIC = "GEMM TFLOP/s and % of MI355X dense MFMA peak (bf16 4096^3)"
 
@@ -169,7 +171,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.in_dtype == gw.BF16 else "f16",
+        "dtype": gw.DTYPE_NAME[w.in_dtype],
         "data": "synthetic",
         "config": {
             "workload": w.name, "M": w.M, "N": w.N, "K": w.K,

@@ -10,7 +10,8 @@ Storage codes are those of the page "gizml:tile" (Constants): F32 = 0,
 F16 = 4, BF16 = 5, FP8 = 9 (E4M3 operands: torch's float8_e4m3fn, the OCP
 format).
 
-The five workloads:
+The workloads (the first five are the method's configurations; the sixth
+is the FP8 operand path at the headline's size):
 
 * ``int_fp16_256``   -- fp16 256^3, integer entries in [-4, 4] (inclusive),
   relu, fp32 out.  Every partial sum is an integer below 2^24, so the fp32
@@ -25,6 +26,8 @@ The five workloads:
   a tile multiple.
 * ``deepk_bf16_2048x16384`` -- bf16 M = N = 2048, K = 16384, N(0, 1), no
   epilogue, bf16 out.
+* ``fp8_4096_relu`` -- FP8 E4M3 4096^3, N(0, 1) rounded to E4M3, relu, bf16
+  out.
 """
 from __future__ import annotations
 
@@ -104,6 +107,7 @@ WORKLOADS = {
         Workload("ragged_fp16_1000", 1000, 1000, 1000, F16, F32, EPI_RELU, 4, UNIT, UNIT),
         Workload("deepk_bf16_2048x16384", 2048, 2048, 16384, BF16, BF16, EPI_NONE, 5, NORMAL,
                  NORMAL),
+        Workload("fp8_4096_relu", 4096, 4096, 4096, FP8, BF16, EPI_RELU, 6, NORMAL, NORMAL),
     ]
 }
 

@@ -50,8 +50,10 @@
 extern "C" {
 #endif
 
-/* Storage codes (page "gizml:tile", Constants). */
-enum { GEMM_F32 = 0, GEMM_F16 = 4, GEMM_BF16 = 5 };
+/* Storage codes (page "gizml:tile", Constants).  FP8 is E4M3, read as the
+ * OCP 8-bit format (bias 7, no infinities, NaN at S.1111.111, largest 448);
+ * it is an operand type only (A and B), outputs are F32, F16 or BF16. */
+enum { GEMM_F32 = 0, GEMM_F16 = 4, GEMM_BF16 = 5, GEMM_FP8 = 9 };
 
 /* Activations applied after the optional bias (page "gizml:tile": Tile.relu,
  * Tile.gelu, Tile.geluErf, Tile.sigmoid, Tile.tanh):
@@ -116,12 +118,13 @@ enum {
 /* The problem.  M, N >= 0, K >= 0 (K == 0 gives C = epilogue(+0));
  * batch >= 1; with batch > 1, stride_a >= M*K, stride_b >= K*N and
  * stride_c >= M*N.  `tile` selects a tile configuration by id (1 ..
- * gemm_tile_count()), or 0 for the planner's choice.  `split_k` cuts K into
+ * gemm_tile_count()), or 0 for the planner's choice; tiles 1-7 take 16-bit
+ * operands and tiles 8-10 FP8 operands (another gives GEMM_E_ARG).  `split_k` cuts K into
  * that many ranges (1 .. 256; fewer if K has fewer trips), or 0 for one
  * range unless GEMM_FLAG_SPLIT_K lets the planner choose. */
 typedef struct gemm_desc {
   int64_t M, N, K;
-  int32_t in_dtype;  /* GEMM_F16 or GEMM_BF16 (A and B)      */
+  int32_t in_dtype;  /* GEMM_F16, GEMM_BF16 or GEMM_FP8 (A and B) */
   int32_t out_dtype; /* GEMM_F32, GEMM_F16 or GEMM_BF16 (C)   */
   int32_t epilogue;  /* GEMM_EPI_* activation                   */
   int32_t flags;     /* GEMM_FLAG_* bits                       */
@@ -196,6 +199,7 @@ typedef struct gemm_run_args {
  * Launch C = epilogue(A . B) on `stream` (a hipStream_t; NULL = the null
  * stream).  A, B, C are device pointers owned by the caller, aligned to
  * their element size; 16-byte-aligned A and B with K and N multiples of 8
+ * (16 for FP8: whole 16-byte chunks)
  * take the 16-byte copy path, others take the element path (same bits).
  * Only C's M x N region of each batch item is written.  Returns
  * GEMM_E_ALIAS if C's extent overlaps A's or B's, GEMM_E_DEVICE if the

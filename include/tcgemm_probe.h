@@ -69,6 +69,25 @@ int tcg_probe_buffer_lds(const uint32_t* src_dev, uint32_t num_records,
                          const uint32_t* lane_voffset_host, uint32_t lds_byte_base,
                          uint32_t* out_dev, void* stream);
 
+/*
+ * One wave runs one v_mfma_f32_32x32x64_f8f6f4 with both operands in FP8
+ * E4M3 (format code 0), no scaling and a zero accumulator.  a_regs_dev and
+ * b_regs_dev hold, per lane (64), the 32 operand bytes of that lane's 8
+ * source registers (lane-major: [64][32], byte 4i+q is byte q of register
+ * i); d_regs_dev receives per lane the 16 fp32 result registers ([64][16]).
+ */
+int tcg_probe_mfma_f8(const uint8_t* a_regs_dev, const uint8_t* b_regs_dev, float* d_regs_dev, void* stream);
+
+/*
+ * ds_read_b64_tr_b8: the LDS buffer (16 KiB) is filled from lds_init_dev
+ * (n_bytes bytes, n_bytes <= 16384), then each lane of one wave issues the
+ * transposing read at its byte address lane_byte_addr_host[lane] (8-byte
+ * aligned, + 8 <= 16384).  out_dev receives the 8 bytes each lane gets back
+ * ([64][8], byte 4i+q is byte q of result register i).
+ */
+int tcg_probe_ds_read_tr8(const uint8_t* lds_init_dev, int n_bytes, const uint32_t* lane_byte_addr_host,
+                          uint8_t* out_dev, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import torch
 
-from .capi import (BF16, EPI_GELU, EPI_GELU_ERF, EPI_NONE, EPI_RELU, EPI_SIGMOID, EPI_TANH, F16,
+from .capi import (BF16, FP8, EPI_GELU, EPI_GELU_ERF, EPI_NONE, EPI_RELU, EPI_SIGMOID, EPI_TANH, F16,
                    F32, FLAG_BIAS, FLAG_FORCE_STAGES_1, FLAG_FORCE_STAGES_2, FLAG_SPLIT_K,
                    FLAG_TUNED, FLAG_UNSTAGED, gemm_autotune, gemm_tune_cache_clear,
                    gemm_tune_cache_load, gemm_tune_cache_save, gemm_tune_cache_size, GEMM_E_ALIAS, GEMM_E_ALIGN, GEMM_E_ARG, GEMM_E_DEVICE,
@@ -55,19 +55,19 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
            stream=None) -> torch.Tensor:
     """C = act(A @ B + bias) with fp32 accumulation on the MFMA units.
 
-    A is [M, K] or [batch, M, K], B is [K, N] or [batch, K, N]; both fp16 or
-    both bf16, row-major and contiguous, on the GPU.  bias is an fp32 vector
+    A is [M, K] or [batch, M, K], B is [K, N] or [batch, K, N]; both fp16,
+    both bf16 or both float8_e4m3fn, row-major and contiguous, on the GPU.  bias is an fp32 vector
     of N values (one per column, shared by every row and batch item).  act is
     None, "relu", "gelu" (tanh form), "gelu_erf", "sigmoid" or "tanh"
     (relu=True means act="relu").  out_dtype is torch.float32, float16 or
-    bfloat16 (default: the input type).  split_k > 1 (or flags with
+    bfloat16 (default: the input type, bfloat16 for FP8 inputs).  split_k > 1 (or flags with
     FLAG_SPLIT_K) splits K; the workspace comes from torch's allocator.
     tune=True measures the configurations (split ones too) the first time a
     problem is seen and keeps the fastest (gemm_autotune); the run that
     tunes writes `out` several times.
     """
-    if A.dtype not in (torch.float16, torch.bfloat16) or B.dtype != A.dtype:
-        raise TypeError("A and B must share one dtype, float16 or bfloat16")
+    if A.dtype not in (torch.float16, torch.bfloat16, torch.float8_e4m3fn) or B.dtype != A.dtype:
+        raise TypeError("A and B must share one dtype, float16, bfloat16 or float8_e4m3fn")
     if not (A.is_cuda and B.is_cuda) or A.device != B.device:
         raise ValueError("A and B must be on the same GPU")
     if not (A.is_contiguous() and B.is_contiguous()):
@@ -81,8 +81,8 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
     K2, N = B.shape[-2], B.shape[-1]
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    odt = out_dtype or A.dtype
-    if odt not in TORCH_TO_CODE:
+    odt = out_dtype or (torch.bfloat16 if A.dtype == torch.float8_e4m3fn else A.dtype)
+    if odt not in (torch.float32, torch.float16, torch.bfloat16):
         raise TypeError("out_dtype must be float32, float16 or bfloat16")
     if act not in _ACT:
         raise ValueError(f"unknown activation {act!r}")

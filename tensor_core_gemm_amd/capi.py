@@ -13,7 +13,7 @@ import torch
 
 from ._lib import lib
 
-F32, F16, BF16 = 0, 4, 5
+F32, F16, BF16, FP8 = 0, 4, 5, 9
 EPI_NONE, EPI_RELU, EPI_GELU, EPI_GELU_ERF, EPI_SIGMOID, EPI_TANH = 0, 1, 2, 3, 4, 5
 FLAG_FORCE_STAGES_1, FLAG_UNSTAGED, FLAG_FORCE_STAGES_2, FLAG_BIAS, FLAG_SPLIT_K = 1, 2, 4, 8, 16
 FLAG_TUNED = 32
@@ -23,7 +23,8 @@ GEMM_E_ARG, GEMM_E_DTYPE, GEMM_E_ALIGN, GEMM_E_ALIAS = -1, -2, -3, -4
 GEMM_E_DEVICE, GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE = -5, -6, -7, -8, -9
 GEMM_E_WORKSPACE = -10
 
-TORCH_TO_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+TORCH_TO_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
+                 torch.float8_e4m3fn: FP8}
 CODE_TO_TORCH = {v: k for k, v in TORCH_TO_CODE.items()}
 
 

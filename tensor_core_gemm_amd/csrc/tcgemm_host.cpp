@@ -41,6 +41,7 @@ bool log_enabled() {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int out_size(int dtype) { return dtype == GEMM_F32 ? 4 : 2; }
+int in_size(int dtype) { return dtype == GEMM_FP8 ? 1 : 2; }
 
 const tcg::TileDesc& tile_desc(int id) { return tcg::kTiles[id - 1]; }
 
@@ -67,7 +68,7 @@ bool is_gfx950(const gemm_device_caps& c) { return std::strncmp(c.arch, "gfx950"
 int validate_desc(const gemm_desc* d) {
   if (!d) return GEMM_E_ARG;
   if (d->M < 0 || d->N < 0 || d->K < 0 || d->batch < 1) return GEMM_E_ARG;
-  if (d->in_dtype != GEMM_F16 && d->in_dtype != GEMM_BF16) return GEMM_E_DTYPE;
+  if (d->in_dtype != GEMM_F16 && d->in_dtype != GEMM_BF16 && d->in_dtype != GEMM_FP8) return GEMM_E_DTYPE;
   if (d->out_dtype != GEMM_F32 && d->out_dtype != GEMM_F16 && d->out_dtype != GEMM_BF16)
     return GEMM_E_DTYPE;
   if (d->epilogue < GEMM_EPI_NONE || d->epilogue > GEMM_EPI_TANH) return GEMM_E_ARG;
@@ -75,6 +76,8 @@ int validate_desc(const gemm_desc* d) {
                    GEMM_FLAG_BIAS | GEMM_FLAG_SPLIT_K | GEMM_FLAG_TUNED))
     return GEMM_E_ARG;
   if (d->tile < 0 || d->tile > tcg::kNumTiles) return GEMM_E_ARG;
+  // A tile is built for one operand width: 16-bit tiles for F16/BF16, 8-bit for FP8.
+  if (d->tile && tcg::kTiles[d->tile - 1].esize != in_size(d->in_dtype)) return GEMM_E_ARG;
   if (d->split_k < 0 || d->split_k > kMaxSplits) return GEMM_E_ARG;
   if (d->batch > 1) {
     if (d->stride_a < d->M * d->K || d->stride_b < d->K * d->N || d->stride_c < d->M * d->N)
@@ -89,9 +92,9 @@ int validate_desc(const gemm_desc* d) {
 // workgroups.
 double tile_efficiency(int id) {
   switch (id) {
-    case 1: return 1.00;
-    case 2: return 0.78;
-    case 3: return 0.45;
+    case 1: case 8: return 1.00;
+    case 2: case 9: return 0.78;
+    case 3: case 10: return 0.45;
     default: return 0.50;
   }
 }
@@ -116,7 +119,10 @@ double estimate_us(const gemm_desc& d, const gemm_device_caps& caps, int id, int
   const int64_t ranges = cdiv(trips, tps);
   const int64_t wgs = cdiv(d.M, t.bm) * cdiv(d.N, t.bn) * d.batch * ranges;
   const int64_t rounds = cdiv(std::max<int64_t>(wgs, 1), std::max(caps.num_cus, 1));
-  const double trip_us = kTrip1Us * ((double)t.bm * t.bn * t.bk / (256.0 * 256.0 * 64.0)) / tile_efficiency(id);
+  // FP8 MFMAs do twice the multiply-adds per cycle of the 16-bit ones.
+  const double rate = t.esize == 1 ? 2.0 : 1.0;
+  const double trip_us =
+      kTrip1Us * ((double)t.bm * t.bn * t.bk / (256.0 * 256.0 * 64.0)) / rate / tile_efficiency(id);
   double us = (double)rounds * (double)(tps + 1) * trip_us;
   if (ranges > 1) {
     const double mn = (double)d.M * (double)d.N * (double)d.batch;
@@ -133,18 +139,20 @@ constexpr int64_t kMinTripsPerSplit = 8;
 // products whose N is a multiple of 96 take the 256 x 96 tile (few trips,
 // many workgroups to stream A and C; measured faster than one 128 x 288 tile
 // per row block); the rest take the general tile and split with the lowest
-// estimated time.  The deeper-ring tiles (6, 7) are selected by id.
+// estimated time.  The deeper-ring tiles (6, 7) are selected by id.  FP8
+// operands choose among their own tiles (8, 9, 10).
 void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, int* tile, int64_t* splits) {
   *splits = 1;
+  const bool fp8 = d.in_dtype == GEMM_FP8;
   if (d.tile) {
     *tile = d.tile;
     if (!may_split) return;
-  } else if (d.K <= 128 && d.N > 0 && d.N % 96 == 0) {
+  } else if (!fp8 && d.K <= 128 && d.N > 0 && d.N % 96 == 0) {
     *tile = 4;
     return;
   }
   double best_t = 1e300;
-  const int lo = d.tile ? d.tile : 1, hi = d.tile ? d.tile : 3;
+  const int lo = d.tile ? d.tile : (fp8 ? 8 : 1), hi = d.tile ? d.tile : (fp8 ? 10 : 3);
   for (int id = lo; id <= hi; ++id) {
     const int64_t trips = cdiv(d.K, tile_desc(id).bk);
     for (int64_t sp = 1; sp <= kMaxSplits; sp *= 2) {
@@ -293,7 +301,7 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
   }
   const auto& t = tile_desc(id);
 
-  const int64_t tiles[2] = {(int64_t)t.bm * t.bk * 2, (int64_t)t.bk * t.bn * 2};
+  const int64_t tiles[2] = {(int64_t)t.bm * t.bk * t.esize, (int64_t)t.bk * t.bn * t.esize};
   int stages = gemm_stage_depth(caps, 0, tiles, 2, (d.flags & GEMM_FLAG_UNSTAGED) ? 0 : 1);
   // Where two stages fit and the tile's kernel is built for a deeper ring,
   // keep more chunks in flight while they fit: more stages hide longer
@@ -309,8 +317,8 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
   while (stages > 0 && tcg::lds_bytes_for(t, stages) > caps->lds_bytes) --stages;
   if (tcg::lds_bytes_for(t, stages) > caps->lds_bytes) return GEMM_E_DEVICE;
   // Byte offsets inside one trip's tiles are 32-bit buffer offsets.
-  if ((int64_t)t.bm * std::max<int64_t>(d.K, 1) * 2 >= (int64_t)0x7fffffff ||
-      (int64_t)t.bk * std::max<int64_t>(d.N, 1) * 2 >= (int64_t)0x7fffffff)
+  if ((int64_t)t.bm * std::max<int64_t>(d.K, 1) * t.esize >= (int64_t)0x7fffffff ||
+      (int64_t)t.bk * std::max<int64_t>(d.N, 1) * t.esize >= (int64_t)0x7fffffff)
     return GEMM_E_SIZE;
   const int64_t tiles_m = cdiv(d.M, t.bm), tiles_n = cdiv(d.N, t.bn);
   const int64_t trips = cdiv(d.K, t.bk);
@@ -335,16 +343,17 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
   in.waves = t.wm * t.wn;
   in.stages = stages;
   in.lds_bytes = tcg::lds_bytes_for(t, stages);
-  in.vec16 = (d.K % 8 == 0 && d.N % 8 == 0 && d.stride_a % 8 == 0 && d.stride_b % 8 == 0) ? 1 : 0;
+  const int64_t epc = 16 / t.esize;  // elements per 16-byte copy
+  in.vec16 = (d.K % epc == 0 && d.N % epc == 0 && d.stride_a % epc == 0 && d.stride_b % epc == 0) ? 1 : 0;
   in.tiles_m = tiles_m;
   in.tiles_n = tiles_n;
   in.workgroups = wgs;
   in.trips = trips;
   const int fm = t.bm / t.wm / tcg::kMfmaM, fn = t.bn / t.wn / tcg::kMfmaN;
-  in.mfma_per_run = tiles_m * tiles_n * d.batch * in.waves * fm * fn * in.trips * (t.bk / tcg::kMfmaK);
+  in.mfma_per_run = tiles_m * tiles_n * d.batch * in.waves * fm * fn * in.trips * (t.bk / tcg::mfma_k(t));
   in.mfma_m = tcg::kMfmaM;
   in.mfma_n = tcg::kMfmaN;
-  in.mfma_k = tcg::kMfmaK;
+  in.mfma_k = tcg::mfma_k(t);
   in.split_k = (int32_t)splits;
   in.trips_per_split = tps;
   in.workspace_bytes = ws_bytes;
@@ -361,7 +370,8 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
                 id, t.bm, t.bn, t.bk, in.waves, stages, in.lds_bytes, in.vec16 ? "16-byte" : "element",
                 (long long)wgs, (long long)tiles_m, (long long)tiles_n, (long long)d.batch,
                 splits > 1 ? " x splits" : "", (long long)in.trips, in.mfma_m, in.mfma_n, in.mfma_k,
-                d.in_dtype == GEMM_BF16 ? "bf16" : "f16", (long long)in.mfma_per_run,
+                d.in_dtype == GEMM_BF16 ? "bf16" : (d.in_dtype == GEMM_FP8 ? "fp8" : "f16"),
+                (long long)in.mfma_per_run,
                 (d.flags & GEMM_FLAG_BIAS) ? "bias+" : "", kActName[d.epilogue], split_text);
   if (log_enabled()) std::fprintf(stderr, "[tcgemm] plan %lldx%lldx%lld: %s\n", (long long)d.M,
                                   (long long)d.N, (long long)d.K, p->text);
@@ -440,14 +450,16 @@ extern "C" int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void*
   if (d.M == 0 || d.N == 0) return GEMM_OK;
   if (!C || (d.K > 0 && (!A || !B))) return GEMM_E_ARG;
   const int osz = out_size(d.out_dtype);
-  if (((uintptr_t)A & 1u) || ((uintptr_t)B & 1u) || ((uintptr_t)C & (uintptr_t)(osz - 1)))
+  const int isz = in_size(d.in_dtype);
+  if (((uintptr_t)A & (uintptr_t)(isz - 1)) || ((uintptr_t)B & (uintptr_t)(isz - 1)) ||
+      ((uintptr_t)C & (uintptr_t)(osz - 1)))
     return GEMM_E_ALIGN;
   // Written parameters may not overlap the others (page "Module Tolk.Uniform", precondition).
   const uintptr_t c0 = (uintptr_t)C;
   const uintptr_t c1 = c0 + (uintptr_t)(((d.batch - 1) * d.stride_c + d.M * d.N) * osz);
   if (d.K > 0) {
-    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((d.batch - 1) * d.stride_a + d.M * d.K) * 2);
-    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((d.batch - 1) * d.stride_b + d.K * d.N) * 2);
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((d.batch - 1) * d.stride_a + d.M * d.K) * isz);
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((d.batch - 1) * d.stride_b + d.K * d.N) * isz);
     if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return GEMM_E_ALIAS;
     if (ws) {
       const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)in.workspace_bytes;
@@ -470,8 +482,8 @@ extern "C" int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void*
     return GEMM_E_DEVICE;
 
   tcg::KArgs a;
-  a.A = static_cast<const uint16_t*>(A);
-  a.B = static_cast<const uint16_t*>(B);
+  a.A = A;
+  a.B = B;
   a.C = C;
   a.bias = bias;
   a.ws = ws;
@@ -511,6 +523,9 @@ extern "C" int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void*
     case 5: e = (gen ? tcg::launch_t5_gen : tcg::launch_t5)(in.stages, vec16, bf16, a, s); break;
     case 6: e = (gen ? tcg::launch_t6_gen : tcg::launch_t6)(in.stages, vec16, bf16, a, s); break;
     case 7: e = (gen ? tcg::launch_t7_gen : tcg::launch_t7)(in.stages, vec16, bf16, a, s); break;
+    case 8: e = (gen ? tcg::launch_t8_gen : tcg::launch_t8)(in.stages, vec16, bf16, a, s); break;
+    case 9: e = (gen ? tcg::launch_t9_gen : tcg::launch_t9)(in.stages, vec16, bf16, a, s); break;
+    case 10: e = (gen ? tcg::launch_t10_gen : tcg::launch_t10)(in.stages, vec16, bf16, a, s); break;
     default: break;
   }
   if (e == hipSuccess && in.split_k > 1) {
@@ -564,6 +579,7 @@ extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B
   TuneChoice best{0, 1, 1e300};
   rc = GEMM_OK;
   for (int id = lo; id <= hi && rc == GEMM_OK; ++id) {
+    if (tcg::kTiles[id - 1].esize != in_size(base.in_dtype)) continue;  // built for the other width
     int last_split = 0;
     for (int sp = 1; sp <= 16; sp *= 2) {
       if (sp > 1 && !(base.flags & GEMM_FLAG_SPLIT_K)) break;

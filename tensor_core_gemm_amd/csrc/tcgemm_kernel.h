@@ -45,6 +45,9 @@
 namespace tcg {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2v __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -55,6 +58,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2v lds_i32x2;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr uint32_t kOOB = 0x80000000u;  // a byte offset no resource here reaches
@@ -82,9 +86,17 @@ template <int CPR>
 __device__ __forceinline__ int swz_a(int r) {
   return (r >> swz_a_shift<CPR>()) & swizzle_mask(CPR);
 }
-template <int CPR>
+// B with 8-bit elements: a transposing 8-byte read of 32 lanes covers 8
+// rows and two adjacent chunks of each, so the XOR spreads 8 rows over 8
+// chunk pairs: 2(r mod 8).
+template <int CPR, int ES>
 __device__ __forceinline__ int swz_b(int r) {
-  return (2 * (r & 3)) & swizzle_mask(CPR);
+  return ES == 2 ? ((2 * (r & 3)) & swizzle_mask(CPR)) : ((2 * (r & 7)) & swizzle_mask(CPR));
+}
+// Rows after which swz_b repeats.
+template <int ES>
+constexpr int swz_b_period() {
+  return ES == 2 ? 4 : 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -163,8 +175,39 @@ __device__ __forceinline__ f32x16 mfma(const u32x4& src0, const u32x4& src1, con
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, src0),
                                                   __builtin_bit_cast(f16x8, src1), acc, 0, 0, 0);
 }
+// FP8 E4M3 operands (format code 0 for both), no scaling: 32 bytes per
+// lane, k = 32 (lane / 32) + byte for the row (or column) lane mod 32.
+template <bool BF16IN>
+__device__ __forceinline__ f32x16 mfma(const u32x8& src0, const u32x8& src1, const f32x16& acc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, src0),
+                                                         __builtin_bit_cast(i32x8, src1), acc, 0, 0, 0, 0, 0, 0);
+}
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  return (b0 & 0xffu) | ((b1 & 0xffu) << 8) | ((b2 & 0xffu) << 16) | (b3 << 24);
+}
+
+// One operand element of ES bytes through a buffer resource (zero past its end).
+template <int ES>
+__device__ __forceinline__ uint32_t load_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (ES == 2)
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  else
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// n elements (16 bytes' worth per 4 words) packed little-endian into words.
+template <int ES, int NW>
+__device__ __forceinline__ void pack_elems(const uint32_t* e, uint32_t* w) {
+#pragma unroll
+  for (int q = 0; q < NW; ++q) {
+    if constexpr (ES == 2)
+      w[q] = pack2(e[2 * q], e[2 * q + 1]);
+    else
+      w[q] = pack4(e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Where a workgroup works: (K range, batch item, tile row, tile column).
@@ -413,6 +456,10 @@ void gemm_kernel(KArgs a) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK, NW = T::NW, NT = T::NT;
   constexpr int FM = T::FM, FN = T::FN, KS = T::KS, WN = T::WN;
   constexpr int CPR_A = T::CPR_A, CPR_B = T::CPR_B;
+  constexpr int ES = T::ES, EPC = T::EPC, MK = T::MK;
+  // A fragment / B fragment of one MFMA: 8 16-bit or 32 8-bit values per lane.
+  using frag_t = std::conditional_t<ES == 2, u32x4, u32x8>;
+  constexpr int FW = ES == 2 ? 4 : 8;  // words per fragment
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -424,8 +471,8 @@ void gemm_kernel(KArgs a) {
   const int64_t M = a.M, N = a.N, K = a.K;
   const int64_t row0 = tp.tm * BM;
   const int64_t col0 = tp.tn * BN;
-  const uint16_t* Ab = a.A + tp.b * a.stride_a;
-  const uint16_t* Bb = a.B + tp.b * a.stride_b;
+  const char* Ab = (const char*)a.A + tp.b * a.stride_a * ES;
+  const char* Bb = (const char*)a.B + tp.b * a.stride_b * ES;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -448,42 +495,53 @@ void gemm_kernel(KArgs a) {
     smem_epi = (lds_char*)epi_lds;
     for (int t = 0; t < trips; ++t) {
       const int64_t k0 = kbase + (int64_t)t * BK;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + row0 * K + k0, ((M - row0) * K - k0) * 2);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + k0 * N + col0, ((K - k0) * N - col0) * 2);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + (row0 * K + k0) * ES, ((M - row0) * K - k0) * ES);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + (k0 * N + col0) * ES, ((K - k0) * N - col0) * ES);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int kk = s * 16 + 8 * (lane >> 5);  // this lane's first k inside the trip
-        u32x4 af[FM], bfr[FN];
+        // this lane's MK/2 consecutive k inside the trip
+        const int kk = s * MK + (MK / 2) * (lane >> 5);
+        frag_t af[FM], bfr[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int r = wm0 + 32 * i + (lane & 31);
           const bool rok = row0 + r < M;
-          const uint32_t off = (uint32_t)(r * K + kk) * 2u;
+          const uint32_t off = (uint32_t)(r * K + kk) * ES;
           if constexpr (VEC16) {
-            const bool ok = rok && (k0 + kk < K);
-            af[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? off : kOOB, 0, 0);
-          } else {
-            uint32_t e[8];
+            // whole 16-byte chunks (K is a multiple of a chunk)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const bool ok = rok && (k0 + kk + q < K);
-              e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, ok ? off + 2u * q : kOOB, 0, 0);
+            for (int q = 0; q < FW / 4; ++q) {
+              const bool ok = rok && (k0 + kk + q * EPC < K);
+              const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? off + 16u * q : kOOB, 0, 0);
+#pragma unroll
+              for (int w4 = 0; w4 < 4; ++w4) af[i][4 * q + w4] = v[w4];
             }
-            af[i] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+          } else {
+            uint32_t e[MK / 2], wv[FW];
+#pragma unroll
+            for (int q = 0; q < MK / 2; ++q) {
+              const bool ok = rok && (k0 + kk + q < K);
+              e[q] = load_elem<ES>(ra, ok ? off + (uint32_t)(ES * q) : kOOB);
+            }
+            pack_elems<ES, FW>(e, wv);
+#pragma unroll
+            for (int q = 0; q < FW; ++q) af[i][q] = wv[q];
           }
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int c = wn0 + 32 * j + (lane & 31);
           const bool cok = col0 + c < N;
-          uint32_t e[8];
+          uint32_t e[MK / 2], wv[FW];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
+          for (int q = 0; q < MK / 2; ++q) {
             const bool ok = cok && (k0 + kk + q < K);
-            const uint32_t off = (uint32_t)((kk + q) * N + c) * 2u;
-            e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, ok ? off : kOOB, 0, 0);
+            const uint32_t off = (uint32_t)((kk + q) * N + c) * ES;
+            e[q] = load_elem<ES>(rb, ok ? off : kOOB);
           }
-          bfr[j] = u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+          pack_elems<ES, FW>(e, wv);
+#pragma unroll
+          for (int q = 0; q < FW; ++q) bfr[j][q] = wv[q];
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -516,34 +574,34 @@ void gemm_kernel(KArgs a) {
     // (swz_a repeats every swz_a_period rows, swz_b every 4 rows)
     constexpr bool SIMPLE_A = (NT % CPR_A == 0) && ((NT / CPR_A) % swz_a_period<CPR_A>() == 0) &&
                               (T::CH_A % NT == 0);
-    constexpr bool SIMPLE_B = (NT % CPR_B == 0) && ((NT / CPR_B) % 4 == 0) && (T::CH_B % NT == 0);
+    constexpr bool SIMPLE_B = (NT % CPR_B == 0) && ((NT / CPR_B) % swz_b_period<ES>() == 0) && (T::CH_B % NT == 0);
     // Per-lane chunk of round 0 (rounds add NT / CPR rows).
     const int a_r0 = tid / CPR_A;
-    const int a_c80 = 8 * ((tid % CPR_A) ^ swz_a<CPR_A>(a_r0));
-    const uint32_t a_off0 = (uint32_t)(a_r0 * K + a_c80) * 2u;
+    const int a_c80 = EPC * ((tid % CPR_A) ^ swz_a<CPR_A>(a_r0));
+    const uint32_t a_off0 = (uint32_t)(a_r0 * K + a_c80) * ES;
     const int b_r0 = tid / CPR_B;
-    const int b_c80 = 8 * ((tid % CPR_B) ^ swz_b<CPR_B>(b_r0));
-    const uint32_t b_off0 = (uint32_t)(b_r0 * N + b_c80) * 2u;
+    const int b_c80 = EPC * ((tid % CPR_B) ^ swz_b<CPR_B, ES>(b_r0));
+    const uint32_t b_off0 = (uint32_t)(b_r0 * N + b_c80) * ES;
     // Copy chunk (trip) t with element loads (rows not 16-byte aligned).
     auto copy_elements = [&](int t, lds_char* slot) __attribute__((always_inline)) {
       const int64_t k0 = kbase + (int64_t)t * BK;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + row0 * K + k0, ((M - row0) * K - k0) * 2);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + k0 * N + col0, ((K - k0) * N - col0) * 2);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + (row0 * K + k0) * ES, ((M - row0) * K - k0) * ES);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + (k0 * N + col0) * ES, ((K - k0) * N - col0) * ES);
 #pragma unroll
       for (int i = 0; i < T::IA; ++i) {
         if (T::CH_A % NT == 0 || (i * NW + w) * 64 < T::CH_A) {
           const int P = i * NT + tid;
           const int r = P / CPR_A;
-          const int c8 = 8 * ((P % CPR_A) ^ swz_a<CPR_A>(r));
-          const uint32_t off = (uint32_t)(r * K + c8) * 2u;
-          uint32_t e[8];
+          const int ce = EPC * ((P % CPR_A) ^ swz_a<CPR_A>(r));
+          const uint32_t off = (uint32_t)(r * K + ce) * ES;
+          uint32_t e[EPC], wv[4];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const bool ok = k0 + c8 + q < K;
-            e[q] = __builtin_amdgcn_raw_buffer_load_b16(ra, ok ? off + 2u * q : kOOB, 0, 0);
+          for (int q = 0; q < EPC; ++q) {
+            const bool ok = k0 + ce + q < K;
+            e[q] = load_elem<ES>(ra, ok ? off + (uint32_t)(ES * q) : kOOB);
           }
-          *(lds_u32x4*)(slot + (i * NW + w) * 1024 + lane * 16) =
-              u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+          pack_elems<ES, 4>(e, wv);
+          *(lds_u32x4*)(slot + (i * NW + w) * 1024 + lane * 16) = u32x4{wv[0], wv[1], wv[2], wv[3]};
         }
       }
 #pragma unroll
@@ -551,16 +609,16 @@ void gemm_kernel(KArgs a) {
         if (T::CH_B % NT == 0 || (i * NW + w) * 64 < T::CH_B) {
           const int P = i * NT + tid;
           const int r = P / CPR_B;
-          const int c8 = 8 * ((P % CPR_B) ^ swz_b<CPR_B>(r));
-          const uint32_t off = (uint32_t)(r * N + c8) * 2u;
-          uint32_t e[8];
+          const int ce = EPC * ((P % CPR_B) ^ swz_b<CPR_B, ES>(r));
+          const uint32_t off = (uint32_t)(r * N + ce) * ES;
+          uint32_t e[EPC], wv[4];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const bool ok = col0 + c8 + q < N;
-            e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, ok ? off + 2u * q : kOOB, 0, 0);
+          for (int q = 0; q < EPC; ++q) {
+            const bool ok = col0 + ce + q < N;
+            e[q] = load_elem<ES>(rb, ok ? off + (uint32_t)(ES * q) : kOOB);
           }
-          *(lds_u32x4*)(slot + T::A_BYTES + (i * NW + w) * 1024 + lane * 16) =
-              u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
+          pack_elems<ES, 4>(e, wv);
+          *(lds_u32x4*)(slot + T::A_BYTES + (i * NW + w) * 1024 + lane * 16) = u32x4{wv[0], wv[1], wv[2], wv[3]};
         }
       }
     };
@@ -575,8 +633,8 @@ void gemm_kernel(KArgs a) {
       CopyCtx c;
       c.k0 = kbase + (int64_t)t * BK;
       c.ktail = c.k0 + BK > K;
-      c.wa = make_rsrc_words(Ab + row0 * K + c.k0, ((M - row0) * K - c.k0) * 2);
-      c.wb = make_rsrc_words(Bb + c.k0 * N + col0, ((K - c.k0) * N - col0) * 2);
+      c.wa = make_rsrc_words(Ab + (row0 * K + c.k0) * ES, ((M - row0) * K - c.k0) * ES);
+      c.wb = make_rsrc_words(Bb + (c.k0 * N + col0) * ES, ((K - c.k0) * N - col0) * ES);
       return c;
     };
     auto copy_part = [&](const CopyCtx& c, lds_char* slot, int q) __attribute__((always_inline)) {
@@ -587,12 +645,12 @@ void gemm_kernel(KArgs a) {
           uint32_t off;
           if constexpr (SIMPLE_A) {
             c8 = a_c80;
-            off = a_off0 + (uint32_t)(i * (NT / CPR_A) * K * 2);
+            off = a_off0 + (uint32_t)(i * (NT / CPR_A) * K * ES);
           } else {
             const int P = i * NT + tid;
             const int r = P / CPR_A;
-            c8 = 8 * ((P % CPR_A) ^ swz_a<CPR_A>(r));
-            off = (uint32_t)(r * K + c8) * 2u;
+            c8 = EPC * ((P % CPR_A) ^ swz_a<CPR_A>(r));
+            off = (uint32_t)(r * K + c8) * ES;
           }
           lds_char* dst = slot + (i * NW + w) * 1024;
           const uint32_t o = (c.ktail && c.k0 + c8 >= K) ? kOOB : off;
@@ -605,12 +663,12 @@ void gemm_kernel(KArgs a) {
           uint32_t off;
           if constexpr (SIMPLE_B) {
             c8 = b_c80;
-            off = b_off0 + (uint32_t)(i * (NT / CPR_B) * N * 2);
+            off = b_off0 + (uint32_t)(i * (NT / CPR_B) * N * ES);
           } else {
             const int P = i * NT + tid;
             const int r = P / CPR_B;
-            c8 = 8 * ((P % CPR_B) ^ swz_b<CPR_B>(r));
-            off = (uint32_t)(r * N + c8) * 2u;
+            c8 = EPC * ((P % CPR_B) ^ swz_b<CPR_B, ES>(r));
+            off = (uint32_t)(r * N + c8) * ES;
           }
           lds_char* dst = slot + T::A_BYTES + (i * NW + w) * 1024;
           const uint32_t o = (b_ntail && col0 + c8 >= N) ? kOOB : off;
@@ -629,71 +687,89 @@ void gemm_kernel(KArgs a) {
       }
     };
 
-    // Fragments of one k-step (s) from a slot.
+    // Fragments of one k-step (s) from a slot.  Row pitches in the slot:
+    // RA bytes for A, RB bytes for B.
     //
-    // A fragment (block i, k-step s): lane l reads row wm0 + 32i + (l mod 32)
-    // at logical chunk 2s + l/32, i.e. 8 k-contiguous values.  The row's
-    // swizzle depends only on l (wm0 and 32i are multiples of the swizzle
-    // period), so the lane's byte offset is a_base[s] + i * 32 * BK * 2.
-    //
-    // B fragment (block j, k-step s): column (l mod 32) and 8 k-values
-    // 16s + 8(l/32) + e, read as two transposing 4-value reads (h = 0, 1).
-    // ds_read_b64_tr_b16 works on groups of 16 lanes: lane x of a group
-    // receives element x mod 4 of the reads of lanes 4e + x/4, e = 0..3.  So
-    // lane 4e + q reads row e of the group's 4 x 16 block at columns
-    // 4q .. 4q+3, and lane x receives column x.  The row is
+    // 16-bit operands.  A fragment (block i, k-step s): lane l reads row
+    // wm0 + 32i + (l mod 32) at logical chunk 2s + l/32, i.e. 8 k-contiguous
+    // values.  The row's swizzle depends only on l (wm0 and 32i are
+    // multiples of the swizzle period), so the lane's byte offset is
+    // a_base[s] + i * 32 * RA.  B fragment (block j, k-step s): column
+    // (l mod 32) and 8 k-values 16s + 8(l/32) + e, read as two transposing
+    // 4-value reads (h = 0, 1).  ds_read_b64_tr_b16 works on groups of 16
+    // lanes: lane x of a group receives element x mod 4 of the reads of lanes
+    // 4e + x/4, e = 0..3.  So lane 4e + q reads row e of the group's 4 x 16
+    // block at columns 4q .. 4q+3, and lane x receives column x.  The row is
     // 16s + 8(l/32) + 4h + ((l mod 16) / 4), whose swizzle depends only on
-    // l, so the lane's byte offset is b_base[j] + (16s + 4h) * BN * 2.
+    // l, so the lane's byte offset is b_base[j] + (16s + 4h) * RB.
+    //
+    // FP8 operands (the MFMA pairs byte b of A lane l with byte b of B lane
+    // l', l and l' in the same half; k = 32 (l / 32) + b is the order used).
+    // A fragment: row wm0 + 32i + (l mod 32), bytes 64s + 32(l/32) .. +31:
+    // logical chunks 4s + 2(l/32) and the next (two 16-byte reads; the XOR
+    // keeps the pair, so the second is the first with bit 4 flipped).  B
+    // fragment: column c = l mod 32, 32 k-values in four transposing 8-byte
+    // reads t = 0..3.  ds_read_b64_tr_b8 works on groups of 16 lanes: lane x
+    // receives byte x mod 8 of the reads of lanes 2e + x/8, e = 0..7.  So
+    // lane s of a group reads row 8t + s/2 (+ 32(l/32) + 64s_k) at the 8
+    // columns starting 16((l/16) mod 2) + 8(s mod 2) of the block, and lane
+    // x receives column x, rows 8t .. 8t+7 in order.  The swizzle of the row
+    // depends only on l (rows step by 8), so the lane's byte offset is
+    // b_base[j] + (64 s_k + 8t) * RB.
+    constexpr int RA = BK * ES, RB = BN * ES;
     static_assert(32 % swz_a_period<CPR_A>() == 0, "A fragment rows must start on a swizzle period");
     int a_base[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int r = wm0 + (lane & 31);
-      const int c = 2 * s + (lane >> 5);
-      a_base[s] = r * (BK * 2) + ((c ^ swz_a<CPR_A>(r)) * 16);
+      const int c = ES == 2 ? 2 * s + (lane >> 5) : 4 * s + 2 * (lane >> 5);
+      a_base[s] = r * RA + ((c ^ swz_a<CPR_A>(r)) * 16);
     }
     int b_base[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
-      const int colq = wn0 + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      b_base[j] = r * (BN * 2) + (((colq >> 3) ^ swz_b<CPR_B>(r)) * 16) + ((colq >> 2) & 1) * 8;
+      if constexpr (ES == 2) {
+        const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
+        const int colq = wn0 + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        b_base[j] = r * RB + (((colq >> 3) ^ swz_b<CPR_B, ES>(r)) * 16) + ((colq >> 2) & 1) * 8;
+      } else {
+        const int r = 32 * (lane >> 5) + ((lane & 15) >> 1);
+        const int colb = wn0 + 32 * j + 16 * ((lane >> 4) & 1);  // byte column of the 16-byte chunk
+        b_base[j] = r * RB + (((colb >> 4) ^ swz_b<CPR_B, ES>(r)) * 16) + (lane & 1) * 8;
+      }
     }
     struct Frags {
-      u32x4 a[FM], b[FN];
+      frag_t a[FM], b[FN];
+    };
+    // Single fragment reads (read r of a k-step: the A reads first, then
+    // the B reads) and single MFMAs, for hand-interleaving.
+    constexpr int RPA = ES == 2 ? 1 : 2;  // reads per A fragment
+    constexpr int RPB = ES == 2 ? 2 : 4;  // reads per B fragment
+    constexpr int NREADS = RPA * FM + RPB * FN;
+    auto load_one = [&](const lds_char* slot, int s, Frags& f, int r) __attribute__((always_inline)) {
+      if (r < RPA * FM) {
+        const int i = r / RPA, q = r % RPA;
+        const u32x4 v = *(const lds_u32x4*)(slot + ((a_base[s] + i * (32 * RA)) ^ (16 * q)));
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) f.a[i][4 * q + w4] = v[w4];
+      } else {
+        const int j = (r - RPA * FM) / RPB, h = (r - RPA * FM) % RPB;
+        if constexpr (ES == 2) {
+          const lds_char* p = slot + T::A_BYTES + b_base[j] + (16 * s + 4 * h) * RB;
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          f.b[j][2 * h] = pack2((uint16_t)x[0], (uint16_t)x[1]);
+          f.b[j][2 * h + 1] = pack2((uint16_t)x[2], (uint16_t)x[3]);
+        } else {
+          const lds_char* p = slot + T::A_BYTES + b_base[j] + (64 * s + 8 * h) * RB;
+          const i32x2v x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+          f.b[j][2 * h] = (uint32_t)x[0];
+          f.b[j][2 * h + 1] = (uint32_t)x[1];
+        }
+      }
     };
     auto load = [&](const lds_char* slot, int s, Frags& f) __attribute__((always_inline)) {
-      const lds_char* sa = slot;
-      const lds_char* sb = slot + T::A_BYTES;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        f.a[i] = *(const lds_u32x4*)(sa + a_base[s] + i * (32 * BK * 2));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        uint32_t v[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const lds_char* p = sb + b_base[j] + (16 * s + 4 * h) * (BN * 2);
-          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-          v[2 * h] = pack2((uint16_t)x[0], (uint16_t)x[1]);
-          v[2 * h + 1] = pack2((uint16_t)x[2], (uint16_t)x[3]);
-        }
-        f.b[j] = u32x4{v[0], v[1], v[2], v[3]};
-      }
-    };
-    // Single fragment reads (read r of a k-step: A blocks first, then the
-    // two halves of each B block) and single MFMAs, for hand-interleaving.
-    constexpr int NREADS = FM + 2 * FN;
-    auto load_one = [&](const lds_char* slot, int s, Frags& f, int r) __attribute__((always_inline)) {
-      if (r < FM) {
-        f.a[r] = *(const lds_u32x4*)(slot + a_base[s] + r * (32 * BK * 2));
-      } else {
-        const int j = (r - FM) >> 1, h = (r - FM) & 1;
-        const lds_char* p = slot + T::A_BYTES + b_base[j] + (16 * s + 4 * h) * (BN * 2);
-        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-        f.b[j][2 * h] = pack2((uint16_t)x[0], (uint16_t)x[1]);
-        f.b[j][2 * h + 1] = pack2((uint16_t)x[2], (uint16_t)x[3]);
-      }
+      for (int r = 0; r < NREADS; ++r) load_one(slot, s, f, r);
     };
     auto mma_one = [&](const Frags& f, int m) __attribute__((always_inline)) {
       const int i = m / FN, j = m % FN;
@@ -760,14 +836,14 @@ void gemm_kernel(KArgs a) {
           if (s + 1 < KS) {
             load(cur, s + 1, next);
             mma(now);
-            interleave_reads_into_mfmas<FM + 2 * FN, FM * FN>();
+            interleave_reads_into_mfmas<NREADS, FM * FN>();
           } else {
             const int newer = newest_issued(t) - (t + 1);
             wait_newer_and_barrier(newer > 0 ? newer : 0);
             if (t + S < trips) copy(t + S, cur);
             if (t + 1 < trips) load(nxt, 0, next);
             mma(now);
-            interleave_reads_into_mfmas<FM + 2 * FN, FM * FN>();
+            interleave_reads_into_mfmas<NREADS, FM * FN>();
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -878,14 +954,21 @@ hipError_t launch_one(const KArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// FP8 tiles have one MFMA for their one input type; BF16IN is false there.
 template <int TID, bool GEN_EPI>
 hipError_t launch_tile(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s) {
+  constexpr bool kFp8 = Tile<TID>::ES == 1;
 #define TCG_CASE(ST)                                                                  \
   if (stages == ST) {                                                                 \
-    if (vec16) return bf16 ? launch_one<TID, ST, true, true, GEN_EPI>(a, s)           \
-                           : launch_one<TID, ST, true, false, GEN_EPI>(a, s);         \
-    return bf16 ? launch_one<TID, ST, false, true, GEN_EPI>(a, s)                     \
-                : launch_one<TID, ST, false, false, GEN_EPI>(a, s);                   \
+    if constexpr (kFp8) {                                                             \
+      return vec16 ? launch_one<TID, ST, true, false, GEN_EPI>(a, s)                  \
+                   : launch_one<TID, ST, false, false, GEN_EPI>(a, s);                \
+    } else {                                                                          \
+      if (vec16) return bf16 ? launch_one<TID, ST, true, true, GEN_EPI>(a, s)         \
+                             : launch_one<TID, ST, true, false, GEN_EPI>(a, s);       \
+      return bf16 ? launch_one<TID, ST, false, true, GEN_EPI>(a, s)                   \
+                  : launch_one<TID, ST, false, false, GEN_EPI>(a, s);                 \
+    }                                                                                 \
   }
   TCG_CASE(0)
   TCG_CASE(1)

@@ -7,8 +7,8 @@ namespace tcg {
 
 // Kernel arguments (passed by value).
 struct KArgs {
-  const uint16_t* A;
-  const uint16_t* B;
+  const void* A;                         // [batch][M][K] operand elements (2 or 1 bytes)
+  const void* B;                         // [batch][K][N]
   void* C;
   const float* bias;                     // N values added to every row before the activation, or null
   float* ws;                             // split-K partial sums [splits][batch][M][N], or null

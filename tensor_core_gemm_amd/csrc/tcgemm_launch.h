@@ -24,6 +24,12 @@ hipError_t launch_t6(int stages, bool vec16, bool bf16, const KArgs& a, hipStrea
 hipError_t launch_t6_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t7(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t7_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t8(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t8_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t9(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t9_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t10(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t10_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 
 // The split-K reduction (tcgemm_reduce.hip).
 hipError_t launch_splitk_reduce(const RArgs& r, hipStream_t s);

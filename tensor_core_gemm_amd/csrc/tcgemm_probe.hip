@@ -18,6 +18,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 
 struct LaneWords {
   uint32_t v[64];
@@ -57,6 +60,25 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(int kind, const uint16_t
   for (int i = 0; i < 16; ++i) d[l * 16 + i] = out[i];
 }
 
+// One v_mfma_f32_32x32x64_f8f6f4 with both operands in FP8 E4M3 (format
+// code 0) and no scaling: per lane 32 operand bytes each, 16 results.
+__global__ __launch_bounds__(64) void probe_mfma_f8_kernel(const uint8_t* a, const uint8_t* b, float* d) {
+  const int l = threadIdx.x;
+  i32x8 ar, br;
+  for (int i = 0; i < 8; ++i) {
+    uint32_t wa = 0, wb = 0;
+    for (int q = 0; q < 4; ++q) {
+      wa |= (uint32_t)a[l * 32 + 4 * i + q] << (8 * q);
+      wb |= (uint32_t)b[l * 32 + 4 * i + q] << (8 * q);
+    }
+    ar[i] = (int)wa;
+    br[i] = (int)wb;
+  }
+  f32x16 acc = {};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ar, br, acc, 0, 0, 0, 0, 0, 0);
+  for (int i = 0; i < 16; ++i) d[l * 16 + i] = acc[i];
+}
+
 constexpr int kTrLdsBytes = 16384;
 
 __global__ __launch_bounds__(64) void probe_tr16_kernel(const uint16_t* init, int n, LaneWords addr,
@@ -69,6 +91,18 @@ __global__ __launch_bounds__(64) void probe_tr16_kernel(const uint16_t* init, in
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4_t*)((__attribute__((address_space(3))) char*)lds + byte));
   for (int i = 0; i < 4; ++i) out[l * 4 + i] = (uint16_t)r[i];
+}
+
+__global__ __launch_bounds__(64) void probe_tr8_kernel(const uint8_t* init, int n, LaneWords addr,
+                                                       uint8_t* out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kTrLdsBytes];
+  for (int i = threadIdx.x; i < kTrLdsBytes; i += 64) lds[i] = (i < n) ? init[i] : 0;
+  __syncthreads();
+  const int l = threadIdx.x;
+  const uint32_t byte = addr.v[l];  // checked on the host: 8-aligned and in range
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_i32x2_t*)((__attribute__((address_space(3))) char*)lds + byte));
+  for (int i = 0; i < 8; ++i) out[l * 8 + i] = (uint8_t)((uint32_t)r[i >> 2] >> (8 * (i & 3)));
 }
 
 constexpr int kDmaLdsBytes = 8192;
@@ -127,5 +161,28 @@ extern "C" int tcg_probe_buffer_lds(const uint32_t* src_dev, uint32_t num_record
   for (int l = 0; l < 64; ++l) v.v[l] = lane_voffset_host[l];
   hipLaunchKernelGGL(probe_buffer_lds_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, src_dev,
                      num_records, v, lds_byte_base, out_dev);
+  return launch_status();
+}
+
+extern "C" int tcg_probe_mfma_f8(const uint8_t* a_regs_dev, const uint8_t* b_regs_dev, float* d_regs_dev,
+                                 void* stream) {
+  if (!a_regs_dev || !b_regs_dev || !d_regs_dev) return GEMM_E_ARG;
+  hipLaunchKernelGGL(probe_mfma_f8_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, a_regs_dev, b_regs_dev,
+                     d_regs_dev);
+  return launch_status();
+}
+
+extern "C" int tcg_probe_ds_read_tr8(const uint8_t* lds_init_dev, int n_bytes, const uint32_t* lane_byte_addr_host,
+                                     uint8_t* out_dev, void* stream) {
+  if (!lds_init_dev || !lane_byte_addr_host || !out_dev) return GEMM_E_ARG;
+  if (n_bytes < 0 || n_bytes > kTrLdsBytes) return GEMM_E_ARG;
+  LaneWords a;
+  for (int l = 0; l < 64; ++l) {
+    uint32_t v = lane_byte_addr_host[l];
+    if ((v & 7u) != 0 || v + 8u > (uint32_t)kTrLdsBytes) return GEMM_E_ARG;
+    a.v[l] = v;
+  }
+  hipLaunchKernelGGL(probe_tr8_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, lds_init_dev, n_bytes, a,
+                     out_dev);
   return launch_status();
 }

@@ -63,3 +63,27 @@ def buffer_lds(src: torch.Tensor, num_records: int, lane_voffset: np.ndarray,
              out.data_ptr(), _stream()), "tcg_probe_buffer_lds")
     torch.cuda.synchronize()
     return out.cpu().numpy().view(np.uint32)
+
+
+def mfma_f8(a_regs: np.ndarray, b_regs: np.ndarray) -> np.ndarray:
+    """One FP8 E4M3 32x32x64 MFMA: a_regs/b_regs are [64, 32] uint8 per-lane
+    register bytes; returns the [64, 16] float32 result registers."""
+    a = torch.from_numpy(np.ascontiguousarray(a_regs, np.uint8)).cuda()
+    b = torch.from_numpy(np.ascontiguousarray(b_regs, np.uint8)).cuda()
+    d = torch.zeros(64 * 16, dtype=torch.float32, device="cuda")
+    f = _fn("tcg_probe_mfma_f8", [_vp, _vp, _vp, _vp])
+    _check(f(a.data_ptr(), b.data_ptr(), d.data_ptr(), _stream()), "tcg_probe_mfma_f8")
+    torch.cuda.synchronize()
+    return d.cpu().numpy().reshape(64, 16)
+
+
+def ds_read_tr8(lds_init: np.ndarray, lane_byte_addr: np.ndarray) -> np.ndarray:
+    init = torch.from_numpy(np.ascontiguousarray(lds_init, np.uint8)).cuda()
+    addr = np.ascontiguousarray(lane_byte_addr, np.uint32)
+    assert addr.shape == (64,)
+    out = torch.zeros(64 * 8, dtype=torch.uint8, device="cuda")
+    f = _fn("tcg_probe_ds_read_tr8", [_vp, ctypes.c_int, _vp, _vp, _vp])
+    _check(f(init.data_ptr(), init.numel(), addr.ctypes.data_as(_vp), out.data_ptr(), _stream()),
+           "tcg_probe_ds_read_tr8")
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(64, 8)

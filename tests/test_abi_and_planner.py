@@ -147,11 +147,36 @@ def test_degenerate_sizes_plan():
     assert i.trips == 0 and i.mfma_per_run == 0
 
 
+FP8_TILES = (8, 9, 10)
+
+
 def test_every_tile_id_plans():
     for t in range(1, tcg.gemm_tile_count() + 1):
-        i = plan(1000, 1000, 1000, tile=t).info()
+        dt = tcg.FP8 if t in FP8_TILES else BF16
+        i = plan(1000, 1000, 1000, in_dtype=dt, tile=t).info()
         assert i.tile_id == t and i.stages >= 2
         assert i.lds_bytes <= 163840
+        # a tile is built for one operand width
+        with pytest.raises(tcg.GemmError) as e:
+            plan(1000, 1000, 1000, in_dtype=BF16 if t in FP8_TILES else tcg.FP8, tile=t)
+        assert e.value.code == tcg.GEMM_E_ARG
+
+
+def test_fp8_plans():
+    """FP8 E4M3 operands: the 8-bit tiles, 64-deep MFMAs, 16-element copies."""
+    i = plan(4096, 4096, 4096, in_dtype=tcg.FP8).info()
+    assert (i.tile_id, i.bm, i.bn, i.bk, i.stages) == (8, 256, 256, 128, 2)
+    assert i.lds_bytes == 2 * (256 * 128 + 128 * 256) == 131072
+    assert (i.mfma_m, i.mfma_n, i.mfma_k) == (32, 32, 64)
+    assert i.mfma_per_run == 256 * 64 * 32 * 2  # tiles x blocks x trips x k-steps
+    assert i.vec16 == 1
+    assert plan(4096, 4096, 4088, in_dtype=tcg.FP8).info().vec16 == 0  # K not whole 16-byte chunks
+    assert plan(1000, 1000, 1000, in_dtype=tcg.FP8).info().tile_id == 10
+    assert "fp8" in plan(256, 256, 256, in_dtype=tcg.FP8).describe()
+    # FP8 is an operand type only
+    with pytest.raises(tcg.GemmError) as e:
+        plan(64, 64, 64, in_dtype=tcg.FP8, out_dtype=tcg.FP8)
+    assert e.value.code == tcg.GEMM_E_DTYPE
 
 
 def test_deep_ring_follows_lds_budget():

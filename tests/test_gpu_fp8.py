@@ -1,0 +1,106 @@
+"""Parity of the FP8 E4M3 operand path (page "gizml:tile", Constants: FP8,
+"the storage type of FP8 E4M3 floats"; read as the OCP format) on the GPU,
+through the C ABI, against the CPU oracle.  The products of two E4M3
+values are exact in fp32, so the oracle's fp32 fold is the reference as
+for the 16-bit types: bit for bit on integer inputs, within the tolerance
+otherwise, and bit for bit between the staged, one-stage and unstaged
+kernels of one plan."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_workloads as gw
+from gemm_workloads import BF16, EPI_GELU, EPI_NONE, EPI_RELU, F16, F32, FP8
+from gpu_helpers import as_bits, as_values, check_against_oracle, check_sampled, run
+
+pytestmark = pytest.mark.gpu
+
+INT8V = gw.Dist("randint", -8, 8)  # exact in E4M3; |sums| stay far below 2^24 here
+
+
+@pytest.fixture(scope="module")
+def tcg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_core_gemm_amd as t
+    t.check_runtime()
+    return t
+
+
+@pytest.mark.parametrize("tile", [8, 9, 10])
+def test_every_fp8_tile_is_exact_on_integers(tcg, tile):
+    w = gw.custom(300, 288, 1000, FP8, F32, EPI_RELU, INT8V, seed=100 + tile)
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w, tile=tile)
+    assert p.info().tile_id == tile and p.info().vec16 == 0  # K = 1000: not whole chunks
+    check_against_oracle(w, A, B, C)
+    w2 = gw.custom(320, 288, 1024, FP8, F32, EPI_RELU, INT8V, seed=110 + tile)
+    A, B = gw.make_inputs(w2)
+    C, _, p = run(tcg, A, B, w2, tile=tile)
+    assert p.info().vec16 == 1
+    check_against_oracle(w2, A, B, C)
+
+
+@pytest.mark.parametrize("out_dtype", [F32, F16, BF16])
+def test_gaussian_within_tolerance(tcg, out_dtype):
+    w = gw.custom(600, 520, 1100, FP8, out_dtype, EPI_RELU, gw.NORMAL, seed=120 + out_dtype)
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w)
+    check_against_oracle(w, A, B, C)
+    for flags in (tcg.FLAG_UNSTAGED, tcg.FLAG_FORCE_STAGES_1):
+        C2, _, _ = run(tcg, A, B, w, flags=flags, tile=p.info().tile_id)
+        assert np.array_equal(as_bits(C), as_bits(C2)), flags
+
+
+EDGE = [(1, 1, 1), (1, 300, 17), (33, 65, 16), (64, 64, 128), (257, 255, 129), (17, 513, 1000),
+        (96, 96, 8)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+def test_edge_shapes(tcg, M, N, K):
+    for dist in (INT8V, gw.NORMAL):
+        w = gw.custom(M, N, K, FP8, BF16, EPI_RELU, dist, seed=M + N + K)
+        A, B = gw.make_inputs(w)
+        C, _, _ = run(tcg, A, B, w)
+        check_against_oracle(w, A, B, C)
+
+
+def test_misaligned_pointers_take_the_element_path(tcg):
+    w = gw.custom(200, 144, 256, FP8, BF16, EPI_RELU, gw.NORMAL, seed=130)
+    A, B = gw.make_inputs(w)
+    C0, _, p = run(tcg, A, B, w)
+    C1, _, _ = run(tcg, A, B, w, plan=p, a_offset=1, b_offset=3)
+    assert np.array_equal(as_bits(C0), as_bits(C1))
+    check_against_oracle(w, A, B, C0)
+
+
+def test_split_bias_activation_and_batch(tcg):
+    w = gw.custom(150, 96, 2048, FP8, F32, EPI_GELU, gw.Dist("normal", 0.0, 2048 ** -0.25),
+                  seed=131, batch=2)
+    A, B = gw.make_inputs(w)
+    bias = gw.draw_bias(w.N, gw.NORMAL, seed=7)
+    C, _, p = run(tcg, A, B, w, tile=9, split_k=4, bias=bias)
+    assert p.info().split_k == 4
+    check_against_oracle(w, A, B, C, bias=bias)
+    Cu, _, _ = run(tcg, A, B, w, tile=9, split_k=4, bias=bias, flags=tcg.FLAG_UNSTAGED)
+    assert np.array_equal(as_bits(C), as_bits(Cu))
+
+
+def test_full_size_4096_sampled_and_stable(tcg):
+    w = gw.WORKLOADS["fp8_4096_relu"]
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w)
+    assert p.info().tile_id == 8
+    assert np.all(np.isfinite(as_values(C)))
+    check_sampled(w, A, B, C)
+    C2, _, _ = run(tcg, A, B, w, plan=p)
+    assert np.array_equal(as_bits(C), as_bits(C2))
+
+
+def test_matmul_binding_takes_fp8(tcg):
+    w = gw.custom(256, 384, 512, FP8, BF16, EPI_NONE, gw.NORMAL, seed=132)
+    A, B = gw.make_inputs(w)
+    C = tcg.matmul(A.cuda(), B.cuda())
+    torch.cuda.synchronize()
+    assert C.dtype == torch.bfloat16
+    check_against_oracle(w, A, B, C.cpu().reshape(1, w.M, w.N))

@@ -145,3 +145,77 @@ def test_buffer_lds_high_offset_reads_zero(probe):
             assert np.all(got[l] == 0)
         else:
             assert np.array_equal(got[l], 1000 + 4 * l + np.arange(4))
+
+
+def _e4m3(x):
+    """FP8 E4M3 (OCP: bias 7, no infinities) patterns of exactly representable values."""
+    t = torch.tensor(np.asarray(x, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+# Candidate maps (half h = lane // 32, register byte j) -> k of the 64-deep
+# FP8 MFMA operands; the test names the one the hardware follows.
+F8_K_MAPS = {
+    "contiguous": lambda h, j: 32 * h + j,
+    "halves_of_16": lambda h, j: 16 * h + (j % 16) + 32 * (j // 16),
+    "quarters_of_8": lambda h, j: 8 * h + (j % 8) + 16 * (j // 8),
+}
+
+
+def test_mfma_f8_32x32x64_layout(probe):
+    """Which k each operand byte holds, for v_mfma_f32_32x32x64_f8f6f4 with
+    E4M3 operands: A lane l holds row l%32, B lane l column l%32, and D has
+    the bf16 32x32 layout; the k of byte j of lane l is one of F8_K_MAPS."""
+    rng = np.random.default_rng(5)
+    A = rng.integers(-4, 5, (32, 64)).astype(np.float32)
+    B = rng.integers(-4, 5, (64, 32)).astype(np.float32)
+    ref = A @ B
+    want = np.zeros((64, 16), np.float32)
+    for l in range(64):
+        for r in range(16):
+            want[l, r] = ref[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32]
+    found = []
+    for name, kmap in F8_K_MAPS.items():
+        a_regs = np.zeros((64, 32), np.float32)
+        b_regs = np.zeros((64, 32), np.float32)
+        for l in range(64):
+            for j in range(32):
+                k = kmap(l // 32, j)
+                a_regs[l, j] = A[l % 32, k]
+                b_regs[l, j] = B[k, l % 32]
+        d = probe.mfma_f8(_e4m3(a_regs), _e4m3(b_regs))
+        _record(f"mfma_f8_{name}", {"d": d.tolist(), "want": want.tolist()})
+        if np.array_equal(d, want):
+            found.append(name)
+    print("FP8 k maps matching the hardware:", found)
+    # Every consistent map gives A.B: the MFMA pairs byte j of A lane l with
+    # byte j of B lane l' (l, l' in the same half), so only the pairing
+    # matters, and the kernels use the contiguous one.  The exact products
+    # of E4M3 integers also confirm the OCP encoding (bias 7).
+    assert found == list(F8_K_MAPS)
+
+
+def test_ds_read_tr8_permutation(probe):
+    """Lane l reads 8 bytes at byte 8l.  Two fills name the source of every
+    returned byte: one with the source lane (byte i holds i // 8), one with
+    the source byte (i % 8).  Within each group of 16 lanes, lane x receives
+    byte x%8 of the reads of lanes 2e + x//8, e = 0..7."""
+    addr = np.arange(64, dtype=np.uint32) * 8
+    idx = np.arange(512)
+    lane_of = probe.ds_read_tr8((idx // 8).astype(np.uint8), addr)
+    byte_of = probe.ds_read_tr8((idx % 8).astype(np.uint8), addr)
+    _record("tr8", {"lane": lane_of.tolist(), "byte": byte_of.tolist()})
+    print("dst -> (src lane, src byte):")
+    for j in range(64):
+        print(j, list(zip(lane_of[j].tolist(), byte_of[j].tolist())))
+    # measured on gfx950: within each group of 16 lanes, dst(lane x, byte e)
+    # = src(lane 2e + x//8, byte x%8); the FP8 B-fragment loader relies on it
+    want_lane = np.zeros((64, 8), np.int64)
+    want_byte = np.zeros((64, 8), np.int64)
+    for j in range(64):
+        g, x = 16 * (j // 16), j % 16
+        for e in range(8):
+            want_lane[j, e] = g + 2 * e + x // 8
+            want_byte[j, e] = x % 8
+    assert np.array_equal(lane_of.astype(np.int64), want_lane)
+    assert np.array_equal(byte_of.astype(np.int64), want_byte)
