@@ -203,14 +203,26 @@ def main():
 def torch_matmul_time(w, io, warmup, steps, stream):
     """torch.matmul (the vendor BLAS on ROCm) on the same resident inputs,
     timed like the steps above; relu, where the workload has it, is a
-    separate in-place op."""
+    separate in-place op.  FP8 operands go through torch._scaled_mm with
+    unit scales (it wants B column-major: a transposed copy made before
+    timing)."""
     import torch
+    import gemm_workloads as gw
     A, B, C = io
     A2, B2 = A.view(w.M, w.K), B.view(w.K, w.N)
     same_type = C.dtype == A.dtype
+    if w.in_dtype == gw.FP8:
+        Bcm = B2.t().contiguous().t()
+        one = torch.ones((), dtype=torch.float32, device=A.device)
+        try:
+            torch._scaled_mm(A2, Bcm, scale_a=one, scale_b=one, out_dtype=C.dtype)
+        except Exception as e:  # not every build has an FP8 GEMM for this device
+            return {"error": f"{type(e).__name__}: {str(e)[:200]}"}
 
     def step():
-        if same_type:
+        if w.in_dtype == gw.FP8:
+            y = torch._scaled_mm(A2, Bcm, scale_a=one, scale_b=one, out_dtype=C.dtype)
+        elif same_type:
             torch.matmul(A2, B2, out=C)
             y = C
         else:
