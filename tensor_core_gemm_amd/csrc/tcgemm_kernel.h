@@ -771,15 +771,19 @@ void gemm_kernel(KArgs a) {
 #pragma unroll
       for (int r = 0; r < NREADS; ++r) load_one(slot, s, f, r);
     };
+    // MFMA order within a k-step: B block outer, A block inner, so
+    // consecutive MFMAs share their first operand (measured about 2 % faster
+    // than the transposed order on bf16 4096^3).  Each accumulator still
+    // takes its k-steps in ascending order.
     auto mma_one = [&](const Frags& f, int m) __attribute__((always_inline)) {
-      const int i = m / FN, j = m % FN;
+      const int i = m % FM, j = m / FM;
       acc[i][j] = mfma<BF16IN>(f.b[j], f.a[i], acc[i][j]);
     };
     auto mma = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma<BF16IN>(f.b[j], f.a[i], acc[i][j]);
+        for (int i = 0; i < FM; ++i) acc[i][j] = mfma<BF16IN>(f.b[j], f.a[i], acc[i][j]);
     };
     auto wait_all_and_barrier = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
