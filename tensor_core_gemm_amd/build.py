@@ -17,6 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtcgemm.so")
+# A C-ABI client test program (tests/c_abi_check.cpp), linked against the library.
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi_check.cpp")
+C_CLIENT = os.path.join(HERE, "c_abi_check")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -58,6 +61,14 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    if os.path.exists(C_CLIENT_SRC):
+        tmp = C_CLIENT + f".tmp{os.getpid()}"
+        cmd = [HIPCC, "-O2", "-std=c++17", "-I", INCLUDE, C_CLIENT_SRC, "-L", HERE, "-ltcgemm",
+               "-Wl,-rpath,$ORIGIN", "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, C_CLIENT)
     return LIB
 
 
