@@ -64,7 +64,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the GEMM would shard along M or N with no exchange step).", file=sys.stderr)
         sys.exit(2)
 

@@ -22,16 +22,16 @@
  * splits the same way and returns the same bits.
  *
  * Elements outside the matrices read as 0 (In.at) and elements outside C are
- * never written (Out.put: "the rest keeps its values").  The staged kernel
+ * never written (Out.put leaves the rest of C as it was).  The staged kernel
  * and the unstaged kernel of the same plan perform the same MFMA sequence on
  * the same values, so they return the same bits (page "Module Tolk.Stage":
- * staging moves values and never rounds them).
+ * staging copies values unchanged).
  *
  * Layout: A is [batch][M][K], B is [batch][K][N], C is [batch][M][N], all
  * row-major with contiguous rows (row pitch K, N and N elements).  stride_*
  * is the distance in elements between consecutive batch items (ignored when
  * batch == 1).  Storage codes are the page's constants (F32 = 0, F16 = 4,
- * BF16 = 5); A and B share one input type ("operands of one type", Tile.dot).
+ * BF16 = 5); A and B share one input type (Tile.dot multiplies operands of the same type).
  *
  * Threading: plans are immutable after creation and may be used from any
  * thread and on any stream.  gemm_run allocates nothing, never

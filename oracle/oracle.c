@@ -18,7 +18,7 @@
  *             acc = fl32(acc + fl32(f32(A[b,i,k]) * f32(B[b,k,j])))   (Tile.dot: F32)
  *         v = bias ? fl32(acc + bias[j]) : acc          (Tile.add, a [1, N] row broadcast)
  *         y = act(v)                                    (Tile.relu, gelu, geluErf, sigmoid, tanh)
- *         C[b,i,j] = round_to_nearest_even(y, out_dtype) (Tile.to: "as a store and a load")
+ *         C[b,i,j] = round_to_nearest_even(y, out_dtype) (Tile.to: what storing and reloading the type gives)
  *
  * Activations (codes 0 none, 1 relu, 2 gelu, 3 geluErf, 4 sigmoid, 5 tanh)
  * follow their definitions on the page, evaluated in double precision from
@@ -38,7 +38,7 @@
  *   - the output conversion rounds to nearest, ties to even; overflow goes
  *     to +-Inf, NaN stays NaN (quiet), subnormals are kept;
  *   - relu(x) is x when x > 0, else +0: -0 and NaN both give +0, because
- *     max(x, 0) "with a NaN, the other value" is 0 (Tile.maximum);
+ *     max(x, 0) returns the operand that is not NaN (Tile.maximum), i.e. 0;
  *   - K = 0 leaves the zero accumulator: C = epilogue(+0) everywhere;
  *   - the product of two fp16 (or two bf16, or two FP8) values is exact in
  *     fp32 except when it over- or underflows fp32's range, so FMA

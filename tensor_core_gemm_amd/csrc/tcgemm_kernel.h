@@ -2,7 +2,7 @@
 //
 // One kernel template serves three paths that issue the same MFMA sequence
 // on the same values, so their results are bit-identical (page "Module
-// Tolk.Stage": staging moves values and never rounds them):
+// Tolk.Stage": staging copies values unchanged):
 //
 //   STAGES = 2  two LDS slots: chunk t+1 is copied into slot (t+1) mod 2
 //               while slot t mod 2 feeds the MFMAs; one barrier per trip

@@ -6,7 +6,7 @@ broadcasting, Tile.relu, Tile.gelu, Tile.geluErf, Tile.sigmoid, Tile.tanh).
 Split K reassociates the fold over k (ranges summed in ascending order), so
 it is checked bit for bit where the arithmetic is exact (integer operands),
 within the tolerance elsewhere, and every path of one split plan must give
-the same bits (staging moves values and never rounds them).
+the same bits (staging copies values unchanged).
 """
 import math
 
@@ -72,7 +72,7 @@ def _condition(epi, x):
 def test_activations_within_a_few_ulp_on_exact_inputs(tcg, epi):
     """A = I, so each output's fp32 input to the activation is an exact fp16
     value of the grid k / 256 in [-8, 8): the device's fp32 activation is
-    compared with the oracle's.  The page asks for results within 2-3 ulp;
+    compared with the oracle's.  The page puts their error at two to three ulp;
     an fp32 evaluation cannot do better than the rounding of its inner
     argument amplified by the function's condition number k(x) (large in the
     GELU forms' negative tail, where the result decays like e^-(2u)), so the

@@ -1,5 +1,5 @@
 """Parity of the FP8 E4M3 operand path (page "gizml:tile", Constants: FP8,
-"the storage type of FP8 E4M3 floats"; read as the OCP format) on the GPU,
+the FP8 E4M3 storage type, read as the OCP format) on the GPU,
 through the C ABI, against the CPU oracle.  The products of two E4M3
 values are exact in fp32, so the oracle's fp32 fold is the reference as
 for the 16-bit types: bit for bit on integer inputs, within the tolerance

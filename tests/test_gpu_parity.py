@@ -3,7 +3,7 @@
 Bars: bit-exact on integer inputs; max relative error <= 1e-2 (floor at
 0.01 of an output's standard deviation) on Gaussian/uniform inputs; the
 staged kernels equal the unstaged kernel bit for bit (page "Module
-Tolk.Stage": staging moves values and never rounds them); one stage equals
+Tolk.Stage": staging copies values unchanged); one stage equals
 two stages; repeat runs are identical; nothing outside C's M x N region is
 written (page "gizml:tile", Out.put / Program.write).
 """
@@ -175,7 +175,7 @@ def test_batch_strides(tcg):
 @pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7])
 def test_every_tile_gives_the_exact_integer_result(tcg, tile):
     """Every tile configuration computes the same result (page "gizml:tile",
-    tune: every configuration must compute the same result)."""
+    tune requires all configurations to agree)."""
     w = gw.custom(300, 288, 300, F16, F32, EPI_NONE, gw.INT4, seed=11)
     A, B = gw.make_inputs(w)
     C, _, p = run(tcg, A, B, w, tile=tile)

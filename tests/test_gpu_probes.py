@@ -15,11 +15,13 @@ import torch
 
 pytestmark = pytest.mark.gpu
 
-OUT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+# Where to keep what the probes measured (for reading after a failure): a
+# directory named by TCGEMM_PROBE_OUT, if set.
+OUT_DIR = os.environ.get("TCGEMM_PROBE_OUT", "")
 
 
 def _record(name, obj):
-    if os.path.isdir(OUT_DIR):
+    if OUT_DIR and os.path.isdir(OUT_DIR):
         with open(os.path.join(OUT_DIR, f"probe_{name}.json"), "w") as f:
             json.dump(obj, f)
 

@@ -1,5 +1,5 @@
 """Pins of the oracle's FP8 operands (page "gizml:tile", Constants: FP8 =
-9, "the storage type of FP8 E4M3 floats", read as the OCP 8-bit E4M3
+9, the FP8 E4M3 storage type, read as the OCP 8-bit E4M3
 format).  The decode is checked against torch's float8_e4m3fn conversion
 for all 256 patterns and against hand-derived values; products and sums
 against exact integer arithmetic and a brute-force fp32 emulation."""

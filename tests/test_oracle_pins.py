@@ -275,7 +275,7 @@ def test_fp32_within_recursive_summation_bound(in_dtype):
 
 def test_relu_of_nan_and_negative_zero():
     # A row with a NaN gives NaN without the epilogue and +0 with relu
-    # (Tile.maximum: with a NaN, the other value).
+    # (Tile.maximum returns the operand that is not NaN).
     a = np.array([[np.nan, 1.0], [-0.0, 0.0]], np.float32)
     b = np.array([[1.0], [1.0]], np.float32)
     for dt in (F16, BF16):
