@@ -106,7 +106,7 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
             p = _plan_cache.get(key)
             if p is None:
                 tflags = flags | FLAG_SPLIT_K
-                wsb = min(16 * batch * M * N * 4, TUNE_WORKSPACE_CAP)
+                wsb = min(16 * batch * M * N * 4, TUNE_WORKSPACE_CAP)  # sums of up to 16 ranges
                 ws = torch.empty(wsb, dtype=torch.uint8, device=A.device)
                 p = gemm_autotune(make_desc(M, N, K, TORCH_TO_CODE[A.dtype], TORCH_TO_CODE[odt], epi,
                                             tflags, batch, *strides),
