@@ -3,7 +3,9 @@
 
 A step is one gemm_run of the workload over inputs already resident in HBM
 (the planner's plan, split K allowed: a split plan's step is the GEMM and
-its reduction).
+its reduction).  Launched back to back, the first ~100 GEMMs see the clock
+dip and recover as power management reacts; the default 200 warm-up steps
+put the timed steps in the settled state a sustained caller sees.
 Default workload: bf16 M = N = K = 4096, A, B ~ N(0, 1), relu, bf16 out
 (the headline GEMM).  W untimed warm-up steps, then K timed steps between
 two device synchronisations; the average launch duration of the kernel is
@@ -39,8 +41,10 @@ METRIC = "GEMM TFLOP/s and % of MI355X dense MFMA peak (bf16 4096^3)"
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed launches first: back to back, the clock dips for about the first "
+                         "100 launches and then settles (power management), so 200 reach the steady state")
     ap.add_argument("--workload", default="bf16_4096_relu")
     ap.add_argument("--tile", type=int, default=0, help="force a tile configuration id")
     ap.add_argument("--flags", type=int, default=0, help="plan flags (1: one stage, 2: unstaged)")
