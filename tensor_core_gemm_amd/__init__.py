@@ -118,12 +118,13 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
             p = plan_for(M, N, K, TORCH_TO_CODE[A.dtype], TORCH_TO_CODE[odt], epi, flags, batch,
                          *strides, tile, split_k)
         ws_bytes = p.info().workspace_bytes
+        if ws_bytes and isinstance(stream, int):
+            # torch cannot keep a temporary workspace alive for a raw stream
+            raise ValueError("a split-K run on a raw stream needs gemm_run_ex with a workspace")
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device) if ws_bytes else None
         gemm_run_ex(p, A, B, out, bias=bias, workspace=ws, stream=stream)
         if ws is not None and stream is not None:
             # the workspace was allocated for torch's current stream
-            if isinstance(stream, int):
-                raise ValueError("a split-K run on a raw stream needs gemm_run_ex with a workspace")
             ws.record_stream(stream)
     return out
 

@@ -829,10 +829,45 @@ void gemm_kernel(KArgs a) {
         workgroup_barrier();
       };
       auto newest_issued = [&](int t) { return (t + S - 1 < trips ? t + S - 1 : trips - 1); };
-      auto trip = [&](int t, auto J) __attribute__((always_inline)) {
+      // The 16-byte copies of one chunk go out in NPART parts, so that the
+      // address unit never receives a whole chunk's instructions inside one
+      // k-step: part 0 right after the barrier that frees the slot
+      // (interleaved with the last k-step's MFMAs), part p >= 1 with k-step
+      // p - 1 of the next trip.  "pend" marks a trip whose previous trip left
+      // parts 1 .. NPART-1 to issue (chunk t - 1 + S, slot t - 1 mod S).  The
+      // last part must still land before the barrier that publishes its
+      // chunk, S - 2 whole trips plus KS - NPART + 1 k-steps after it
+      // issues.  With two k-steps per trip and two slots a second part
+      // would have a single k-step, too short (measured slower on the
+      // 32-deep 16-bit and the FP8 tiles): there the whole chunk goes out
+      // after the barrier.
+      constexpr bool SPREAD = VEC16 && (KS >= 3 || S >= 3);
+      constexpr int NPART = SPREAD ? 2 : 1;
+      static_assert(NPART <= KS, "every part after the first needs a k-step of the next trip");
+      constexpr int ND = T::IA + T::IB, NM = FM * FN;
+      constexpr int RPM = (NREADS + NM - 1) / NM;
+      // copy instructions [part_lo(p), part_lo(p + 1)) form part p
+      auto part_lo = [](int p) constexpr { return p * ND / NPART; };
+      // Part p of chunk u into slot, one instruction before MFMA m of a
+      // k-step when m is the instruction's share of the k-step.
+      auto copy_part_at = [&](const CopyCtx& c, lds_char* slot, int p, int m) __attribute__((always_inline)) {
+        const int q0 = part_lo(p), n = part_lo(p + 1) - q0;
+#pragma unroll
+        for (int q = 0; q < n; ++q)
+          if (q * NM / n == m) copy_part(c, slot, q0 + q);
+      };
+      auto rest_of_previous = [&](int t, int j) __attribute__((always_inline)) {
+        const CopyCtx c = copy_ctx(t - 1 + S);
+#pragma unroll
+        for (int q = part_lo(1); q < ND; ++q) copy_part(c, ring[(j + S - 1) % S], q);
+      };
+      auto trip = [&](int t, auto J, bool pend) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
         lds_char* cur = ring[j];
         lds_char* nxt = ring[(j + 1) % S];
+        if constexpr (SPREAD) {
+          if (pend) rest_of_previous(t, j);
+        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           Frags& now = (s & 1) ? f1 : f0;
@@ -853,36 +888,46 @@ void gemm_kernel(KArgs a) {
         }
       };
       // The same trip where chunk t+S exists and chunk t+1 follows (every
-      // trip but the last S): the last k-step is interleaved by hand, one
-      // read of the next chunk's first fragments and one copy instruction
-      // between consecutive MFMAs, so the MFMA pipe keeps running while the
-      // refill and the reads issue.
-      auto trip_fast = [&](int t, auto J) __attribute__((always_inline)) {
+      // trip but the last S): the first and the last k-step are interleaved
+      // by hand, fragment reads and copy instructions spread between
+      // consecutive MFMAs, so the MFMA pipe keeps running while they issue.
+      auto trip_fast = [&](int t, auto J, auto PEND) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
+        constexpr bool pend = decltype(PEND)::value;
         lds_char* cur = ring[j];
         lds_char* nxt = ring[(j + 1) % S];
 #pragma unroll
         for (int s = 0; s + 1 < KS; ++s) {
           Frags& now = (s & 1) ? f1 : f0;
           Frags& next = (s & 1) ? f0 : f1;
-          load(cur, s + 1, next);
-          mma(now);
-          interleave_reads_into_mfmas<NREADS, FM * FN>();
-          __builtin_amdgcn_sched_barrier(0);
+          if (pend && s + 1 < NPART) {
+            const CopyCtx c = copy_ctx(t - 1 + S);
+            lds_char* prev = ring[(j + S - 1) % S];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+#pragma unroll
+              for (int r = m * RPM; r < (m + 1) * RPM && r < NREADS; ++r) load_one(cur, s + 1, next, r);
+              copy_part_at(c, prev, s + 1, m);
+              mma_one(now, m);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            load(cur, s + 1, next);
+            mma(now);
+            interleave_reads_into_mfmas<NREADS, FM * FN>();
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         Frags& now = ((KS - 1) & 1) ? f1 : f0;
         Frags& next = ((KS - 1) & 1) ? f0 : f1;
         const int newer = newest_issued(t) - (t + 1);
         wait_newer_and_barrier(newer > 0 ? newer : 0);
         const CopyCtx c = copy_ctx(t + S);
-        constexpr int NM = FM * FN, ND = T::IA + T::IB;
-        constexpr int RPM = (NREADS + NM - 1) / NM, DPM = (ND + NM - 1) / NM;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
 #pragma unroll
           for (int r = m * RPM; r < (m + 1) * RPM && r < NREADS; ++r) load_one(nxt, 0, next, r);
-#pragma unroll
-          for (int q = m * DPM; q < (m + 1) * DPM && q < ND; ++q) copy_part(c, cur, q);
+          copy_part_at(c, cur, 0, m);
           mma_one(now, m);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -899,31 +944,51 @@ void gemm_kernel(KArgs a) {
       // last trips are peeled so the loop body has no branch around a whole
       // trip.  KS is even, so every trip starts with its fragments in f0.
       static_assert(KS % 2 == 0, "k-steps per trip must be even");
+      static_assert(KS >= 2, "the first k-step of a fast trip is not its last");
       using I0 = std::integral_constant<int, 0>;
       using I1 = std::integral_constant<int, 1>;
       using I2 = std::integral_constant<int, 2>;
       using I3 = std::integral_constant<int, 3>;
+      using Yes = std::true_type;
+      using No = std::false_type;
       int t = 0;
-      if constexpr (VEC16) {
+      bool pend = false;
+      if constexpr (SPREAD) {
+        // the first fast trip has no parts of an earlier chunk to issue
+        if (2 * S <= trips) {
+          trip_fast(0, I0{}, No{});
+          trip_fast(1, I1{}, Yes{});
+          if constexpr (S >= 3) trip_fast(2, I2{}, Yes{});
+          if constexpr (S >= 4) trip_fast(3, I3{}, Yes{});
+          for (t = S; t + 2 * S <= trips; t += S) {
+            trip_fast(t, I0{}, Yes{});
+            trip_fast(t + 1, I1{}, Yes{});
+            if constexpr (S >= 3) trip_fast(t + 2, I2{}, Yes{});
+            if constexpr (S >= 4) trip_fast(t + 3, I3{}, Yes{});
+          }
+          pend = true;
+        }
+      } else if constexpr (VEC16) {
         for (; t + 2 * S <= trips; t += S) {
-          trip_fast(t, I0{});
-          trip_fast(t + 1, I1{});
-          if constexpr (S >= 3) trip_fast(t + 2, I2{});
-          if constexpr (S >= 4) trip_fast(t + 3, I3{});
+          trip_fast(t, I0{}, No{});
+          trip_fast(t + 1, I1{}, No{});
+          if constexpr (S >= 3) trip_fast(t + 2, I2{}, No{});
+          if constexpr (S >= 4) trip_fast(t + 3, I3{}, No{});
         }
       }
       for (; t + S <= trips; t += S) {
-        trip(t, I0{});
-        trip(t + 1, I1{});
-        if constexpr (S >= 3) trip(t + 2, I2{});
-        if constexpr (S >= 4) trip(t + 3, I3{});
+        trip(t, I0{}, pend);
+        trip(t + 1, I1{}, false);
+        if constexpr (S >= 3) trip(t + 2, I2{}, false);
+        if constexpr (S >= 4) trip(t + 3, I3{}, false);
+        pend = false;
       }
-      if (t < trips) trip(t, I0{});
+      if (t < trips) trip(t, I0{}, pend);
       if constexpr (S >= 3) {
-        if (t + 1 < trips) trip(t + 1, I1{});
+        if (t + 1 < trips) trip(t + 1, I1{}, false);
       }
       if constexpr (S >= 4) {
-        if (t + 2 < trips) trip(t + 2, I2{});
+        if (t + 2 < trips) trip(t + 2, I2{}, false);
       }
     } else {
       for (int t = 0; t < trips; ++t) {
