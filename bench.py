@@ -223,27 +223,38 @@ def torch_matmul_time(w, io, warmup, steps, stream):
         except Exception as e:  # not every build has an FP8 GEMM for this device
             return {"error": f"{type(e).__name__}: {str(e)[:200]}"}
 
-    def step():
+    def gemm():
         if w.in_dtype == gw.FP8:
-            y = torch._scaled_mm(A2, Bcm, scale_a=one, scale_b=one, out_dtype=C.dtype)
-        elif same_type:
+            return torch._scaled_mm(A2, Bcm, scale_a=one, scale_b=one, out_dtype=C.dtype)
+        if same_type:
             torch.matmul(A2, B2, out=C)
-            y = C
-        else:
-            y = torch.matmul(A2, B2).to(C.dtype)
+            return C
+        return torch.matmul(A2, B2).to(C.dtype)
+
+    def step():
+        y = gemm()
         if w.epilogue:
             torch.relu_(y)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    return {"ms_per_step": round(ms, 5), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2),
-            "with_relu": bool(w.epilogue)}
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    ms = timed(step)
+    out = {"ms_per_step": round(ms, 5), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2),
+           "with_relu": bool(w.epilogue)}
+    if w.epilogue:
+        # the product alone, without the separate relu
+        ms_gemm = timed(gemm)
+        out["gemm_only_ms"] = round(ms_gemm, 5)
+        out["gemm_only_tflops"] = round(w.flops / (ms_gemm * 1e-3) / 1e12, 2)
+    return out
 
 
 def kernel_source_sha() -> str:
