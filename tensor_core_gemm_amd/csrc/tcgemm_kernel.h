@@ -255,6 +255,20 @@ struct OutRef {
   int vec4, vec16;    // aligned 4-element / 16-byte stores allowed
 };
 
+// Whole-vector output stores.  Tiles that run one workgroup per CU write
+// their 16-bit outputs with the non-temporal hint: measured 1-2 % faster on
+// 4096^3 (bf16 and FP8), where every tile's output leaves at the end of
+// the launch; on the tiles that run several workgroups per CU (the Swin
+// projection) and on split-K partial sums, which the reduction reads back
+// at once, it was slower, so those stores stay plain.
+template <bool NT, class V>
+__device__ __forceinline__ void store_vec(char* dst, const V& v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, (V*)dst);
+  else
+    *(V*)dst = v;
+}
+
 __device__ __forceinline__ OutRef out_ref(const KArgs& a, const TilePos& tp) {
   OutRef o;
   o.M = a.M;
@@ -292,7 +306,7 @@ __device__ __forceinline__ OutRef out_ref(const KArgs& a, const TilePos& tp) {
 // a wave's 64 groups.
 
 // Rounded band (no bias; activation none or relu), OUT the output type.
-template <class T, int OUT>
+template <class T, int OUT, bool NT>
 __device__ __forceinline__ void store_rounded(const OutRef& o, const f32x16 (&acc)[T::FM][T::FN],
                                               int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {
   constexpr int EPW = T::EPW, EPJ = EPW / 32;
@@ -347,7 +361,7 @@ __device__ __forceinline__ void store_rounded(const OutRef& o, const f32x16 (&ac
         if (m >= M || n >= N) continue;
         char* dst = o.C + (m * N + n) * osz;
         if (o.vec16 && n + per_elem <= N) {
-          *(u32x4*)dst = v;
+          store_vec<NT>(dst, v);
         } else {
           const int cnt = (int)((N - n) < per_elem ? (N - n) : per_elem);
           if (osz == 4) {
@@ -362,7 +376,7 @@ __device__ __forceinline__ void store_rounded(const OutRef& o, const f32x16 (&ac
 }
 
 // fp32 band, epilogue on the read-back side (transcendental activations).
-template <class T>
+template <class T, bool NT>
 __device__ __forceinline__ void store_general(const OutRef& o, const f32x16 (&acc)[T::FM][T::FN],
                                               int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {  constexpr int EPW = T::EPW, EPJ = EPW / 32;
   const int64_t M = o.M, N = o.N;
@@ -409,7 +423,7 @@ __device__ __forceinline__ void store_general(const OutRef& o, const f32x16 (&ac
         const bool full = o.vec4 && n + 4 <= N;
         if (o.dtype == kOutF32) {
           if (full) {
-            *(f32x4*)dst = f32x4{y[0], y[1], y[2], y[3]};
+            store_vec<NT>(dst, f32x4{y[0], y[1], y[2], y[3]});
           } else {
             for (int q = 0; q < 4; ++q)
               if (n + q < N) ((float*)dst)[q] = y[q];
@@ -419,7 +433,7 @@ __device__ __forceinline__ void store_general(const OutRef& o, const f32x16 (&ac
 #pragma unroll
           for (int q = 0; q < 4; ++q) h[q] = to_out16(y[q], o.dtype);
           if (full) {
-            *(u32x2*)dst = u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+            store_vec<NT>(dst, u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])});
           } else {
             for (int q = 0; q < 4; ++q)
               if (n + q < N) ((uint16_t*)dst)[q] = h[q];
@@ -433,15 +447,18 @@ __device__ __forceinline__ void store_general(const OutRef& o, const f32x16 (&ac
 template <class T, bool GEN_EPI>
 __device__ __forceinline__ void store_through_lds(const OutRef& o, const f32x16 (&acc)[T::FM][T::FN],
                                                   int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {
+  constexpr bool NT = T::MIN_WAVES == 1;  // see store_vec
   if constexpr (GEN_EPI) {
-    store_general<T>(o, acc, m0, n0, lane, w, smem);
+    store_general<T, NT>(o, acc, m0, n0, lane, w, smem);  // never split partial sums
   } else {
+    // fp32 bands: split partial sums, and fp32 outputs (not measured
+    // with the hint; one instantiation serves both)
     if (o.dtype == kOutF32)
-      store_rounded<T, kOutF32>(o, acc, m0, n0, lane, w, smem);
+      store_rounded<T, kOutF32, false>(o, acc, m0, n0, lane, w, smem);
     else if (o.dtype == kOutBF16)
-      store_rounded<T, kOutBF16>(o, acc, m0, n0, lane, w, smem);
+      store_rounded<T, kOutBF16, NT>(o, acc, m0, n0, lane, w, smem);
     else
-      store_rounded<T, kOutF16>(o, acc, m0, n0, lane, w, smem);
+      store_rounded<T, kOutF16, NT>(o, acc, m0, n0, lane, w, smem);
   }
 }
 
