@@ -183,6 +183,30 @@ def test_every_tile_gives_the_exact_integer_result(tcg, tile):
     check_against_oracle(w, A, B, C)
 
 
+# Trip counts around the copy schedule's boundaries: a ring of S slots runs
+# the hand-interleaved trips only while chunk t + 2S exists, and then splits
+# each chunk's copies between two trips; the last trips issue whole chunks
+# and finish a split one.  K = BK * trips - 8 leaves a partial last chunk.
+TRIP_CASES = [(tile, trips, flags) for tile, flags in ((1, 0), (2, 0), (3, 0), (6, 0), (7, 0),
+                                                       (6, "stages2"), (7, "stages2"))
+              for trips in range(1, 10)]
+
+
+@pytest.mark.parametrize("tile,trips,flags", TRIP_CASES)
+def test_trip_counts_across_the_copy_schedule(tcg, tile, trips, flags):
+    bk = 64 if tile in (1, 2, 3) else 32
+    K = bk * trips - 8
+    f = tcg.FLAG_FORCE_STAGES_2 if flags == "stages2" else 0
+    w = gw.custom(300, 264, K, F16, F32, EPI_RELU, gw.INT4, seed=100 * tile + trips)
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w, tile=tile, flags=f)
+    info = p.info()
+    assert info.tile_id == tile and info.trips == trips
+    if flags == "stages2":
+        assert info.stages == 2
+    check_against_oracle(w, A, B, C)
+
+
 EDGE = [(1, 1, 1), (1, 300, 17), (300, 1, 64), (33, 65, 16), (64, 64, 64), (257, 255, 129),
         (17, 513, 1000), (96, 96, 8)]
 
