@@ -868,10 +868,12 @@ void gemm_kernel(KArgs a) {
       // Part p of chunk u into slot, one instruction before MFMA m of a
       // k-step when m is the instruction's share of the k-step.
       auto copy_part_at = [&](const CopyCtx& c, lds_char* slot, int p, int m) __attribute__((always_inline)) {
+        // the part's instructions q with q * NM / n == m (rounded down),
+        // computed rather than searched so the unroller sees a small body
         const int q0 = part_lo(p), n = part_lo(p + 1) - q0;
+        const int lo = (m * n + NM - 1) / NM, hi = ((m + 1) * n + NM - 1) / NM;
 #pragma unroll
-        for (int q = 0; q < n; ++q)
-          if (q * NM / n == m) copy_part(c, slot, q0 + q);
+        for (int q = lo; q < hi; ++q) copy_part(c, slot, q0 + q);
       };
       auto rest_of_previous = [&](int t, int j) __attribute__((always_inline)) {
         const CopyCtx c = copy_ctx(t - 1 + S);
