@@ -104,3 +104,17 @@ def test_matmul_binding_takes_fp8(tcg):
     torch.cuda.synchronize()
     assert C.dtype == torch.bfloat16
     check_against_oracle(w, A, B, C.cpu().reshape(1, w.M, w.N))
+
+
+# Trip counts 1..7 on each FP8 tile (two k-steps a trip, so every chunk's
+# copies go out after its barrier), with K one 16-byte chunk short of whole
+# trips so the last chunk is partial.
+@pytest.mark.parametrize("tile", [8, 9, 10])
+@pytest.mark.parametrize("trips", range(1, 8))
+def test_fp8_trip_counts(tcg, tile, trips):
+    K = 128 * trips - 16
+    w = gw.custom(300, 272, K, FP8, BF16, EPI_RELU, INT8V, seed=200 + 10 * tile + trips)
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w, tile=tile)
+    assert p.info().tile_id == tile and p.info().trips == trips and p.info().vec16 == 1
+    check_against_oracle(w, A, B, C)
