@@ -62,7 +62,64 @@ def parse():
                          "the same way, with the activation as a separate op; reported as context")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--planner-sweep", action="store_true",
+                    help="instead of the bench line: for a sweep of bf16 relu shapes, time the "
+                         "planner's choice, the autotuner's and torch.matmul (one JSON line each)")
     return ap.parse_args()
+
+
+# Shapes of the planner sweep: square sizes, skinny and deep-K products.
+SWEEP = [(512, 512, 512), (1024, 1024, 1024), (2048, 2048, 2048), (2304, 2304, 2304),
+         (3000, 3000, 3000), (4096, 4096, 4096), (6144, 6144, 6144), (8192, 8192, 8192),
+         (1024, 4096, 4096), (4096, 1024, 4096), (4096, 4096, 1024), (256, 4096, 4096),
+         (4096, 256, 4096), (128, 8192, 8192), (512, 8192, 8192), (8192, 1024, 1024),
+         (16384, 16384, 1024), (2048, 2048, 8192), (512, 512, 16384), (1024, 1024, 32768)]
+
+
+def planner_sweep():
+    """The planner's choice (splits allowed), the autotuner's and torch.matmul
+    on each SWEEP shape: bf16 operands from N(0,1), relu, bf16 out; HIP
+    events, 30 warm-up launches, best of three runs of 20."""
+    import torch
+
+    import tensor_core_gemm_amd as tcg
+
+    def timed(fn):
+        for _ in range(30):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 20 * 1e3)
+        return best
+
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for M, N, K in SWEEP:
+        A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        B = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+        C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        tflop = 2.0 * M * N * K / 1e12
+        row = {"shape": [M, N, K]}
+        desc = tcg.make_desc(M, N, K, tcg.BF16, tcg.BF16, tcg.EPI_RELU, tcg.FLAG_SPLIT_K)
+        ws = torch.empty(min(16 * M * N * 4, 1 << 30), dtype=torch.uint8, device="cuda")
+        for name, p in (("planner", tcg.gemm_plan(desc)),
+                        ("autotune", tcg.gemm_autotune(desc, A, B, C, workspace=ws))):
+            i = p.info()
+            w = ws if i.workspace_bytes else None
+            us = timed(lambda: tcg.gemm_run_ex(p, A, B, C, workspace=w))
+            row[name] = {"us": round(us, 2), "tflops": round(tflop / us * 1e6, 1),
+                         "tile": i.tile_id, "split": i.split_k}
+        us = timed(lambda: torch.matmul(A, B, out=C))
+        row["torch_matmul"] = {"us": round(us, 2), "tflops": round(tflop / us * 1e6, 1)}
+        print(json.dumps(row), flush=True)
+        del A, B, C, ws
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -81,6 +138,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
     tcg.check_runtime()
+    if args.planner_sweep:
+        planner_sweep()
+        return
     w = gw.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -60,8 +60,11 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
     of N values (one per column, shared by every row and batch item).  act is
     None, "relu", "gelu" (tanh form), "gelu_erf", "sigmoid" or "tanh"
     (relu=True means act="relu").  out_dtype is torch.float32, float16 or
-    bfloat16 (default: the input type, bfloat16 for FP8 inputs).  split_k > 1 (or flags with
-    FLAG_SPLIT_K) splits K; the workspace comes from torch's allocator.
+    bfloat16 (default: the input type, bfloat16 for FP8 inputs).  The planner
+    may split K into ranges where its time model says that pays (deep K, few
+    output tiles; the workspace comes from torch's allocator); split_k = 1
+    forbids it, split_k > 1 asks for that many ranges.  On a raw stream
+    handle the planner does not split unless split_k asks for it.
     tune=True measures the configurations (split ones too) the first time a
     problem is seen and keeps the fastest (gemm_autotune); the run that
     tunes writes `out` several times.
@@ -99,6 +102,8 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
         out = torch.empty(shape, dtype=odt, device=A.device)
     elif tuple(out.shape) != shape or out.dtype != odt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
+    if split_k == 0 and not isinstance(stream, int):
+        flags |= FLAG_SPLIT_K
     with torch.cuda.device(A.device):
         strides = (M * K if batch > 1 else 0, K * N if batch > 1 else 0, M * N if batch > 1 else 0)
         if tune and not tile and not split_k:

@@ -86,48 +86,65 @@ int validate_desc(const gemm_desc* d) {
   return GEMM_OK;
 }
 
-// Relative MFMA throughput of the general tiles on one CU, from timings on
-// MI355X (bf16 4096^3, 2048x2048x16384 and 1000^3): the 256 x 256 tile
-// reuses each LDS byte the most; smaller tiles trade reuse for more
-// workgroups.
-double tile_efficiency(int id) {
+// Time model of the planner, in microseconds, fitted to steady-state timings
+// on MI355X (bf16, a sweep of 20 shapes from 512^3 to 8192^3 and skinny,
+// deep-K and short-K ones; the FP8 tiles move the same bytes per trip as
+// their 16-bit counterparts and cost the same per trip).
+//  - A launch costs kFixedUs plus the time to write C at kStoreBytesPerUs
+//    (the outputs leave at the end of their tiles).
+//  - Workgroups run in rounds of per_cu per CU.  A round that puts two on
+//    some CU costs trip_shared per trip; a round of at most one per CU
+//    costs trip_alone per trip, which for the 256 x 256 tiles grows with
+//    the fraction of CUs busy (from trip_alone at none to trip_shared at
+//    all: the chip runs at its power limit, so fewer busy CUs run faster).
+//  - A split-K run adds its reduction, which moves every partial sum twice
+//    (written by the GEMM, read back) at an effective kReduceBytesPerUs,
+//    plus one launch.  The partial sums mostly stay in the last-level
+//    cache: 2048 x 2048 x 16384 in four ranges measured 14 us of reduction.
+struct TileCost {
+  int per_cu;          // workgroups one CU runs at once
+  double trip_alone;   // us per trip, at most one workgroup per CU
+  double trip_shared;  // us per trip, two per CU (or every CU busy, per_cu = 1)
+  bool power_scaled;   // trip_alone rises to trip_shared with the busy fraction
+};
+TileCost tile_cost(int id) {
   switch (id) {
-    case 1: case 8: return 1.00;
-    case 2: case 9: return 0.78;
-    case 3: case 10: return 0.45;
-    default: return 0.50;
+    case 1: case 8: return {1, 0.93, 1.52, true};
+    case 6: return {1, 0.56, 0.92, true};
+    case 2: case 9: return {2, 0.75, 0.90, false};
+    case 3: case 10: return {2, 0.45, 0.60, false};
+    case 7: return {2, 0.31, 0.54, false};
+    default: return {1, 1.0, 1.0, false};  // 4, 5: chosen by rule or by id
   }
 }
-
-// Time model of the planner, in microseconds, calibrated on MI355X under
-// sustained load: one 256 x 256 x 64 trip of the first tile takes about
-// kTrip1Us with every CU busy; a workgroup also spends about one trip on its
-// prologue and epilogue; workgroups run one per CU; a split-K run adds its
-// reduction, which moves every partial sum twice (written by the GEMM, read
-// back) at an effective kReduceBytesPerUs, plus one launch.  The partial
-// sums mostly stay in the last-level cache: 2048 x 2048 x 16384 in four
-// ranges measured 134 us against 120 us for the same work unsplit, which
-// puts the effective rate near 10 TB/s.
-constexpr double kTrip1Us = 2.0;
+constexpr double kFixedUs = 3.0;
+constexpr double kStoreBytesPerUs = 6.0e6;
 constexpr double kReduceBytesPerUs = 10.0e6;
 constexpr double kLaunchUs = 4.0;
 
 double estimate_us(const gemm_desc& d, const gemm_device_caps& caps, int id, int64_t splits) {
   const auto& t = tile_desc(id);
+  const TileCost c = tile_cost(id);
   const int64_t trips = std::max<int64_t>(cdiv(d.K, t.bk), 1);
   const int64_t tps = cdiv(trips, splits);
   const int64_t ranges = cdiv(trips, tps);
-  const int64_t wgs = cdiv(d.M, t.bm) * cdiv(d.N, t.bn) * d.batch * ranges;
-  const int64_t rounds = cdiv(std::max<int64_t>(wgs, 1), std::max(caps.num_cus, 1));
-  // FP8 MFMAs do twice the multiply-adds per cycle of the 16-bit ones.
-  const double rate = t.esize == 1 ? 2.0 : 1.0;
-  const double trip_us =
-      kTrip1Us * ((double)t.bm * t.bn * t.bk / (256.0 * 256.0 * 64.0)) / rate / tile_efficiency(id);
-  double us = (double)rounds * (double)(tps + 1) * trip_us;
-  if (ranges > 1) {
-    const double mn = (double)d.M * (double)d.N * (double)d.batch;
-    us += (2.0 * ranges * mn * 4.0 + mn * out_size(d.out_dtype)) / kReduceBytesPerUs + kLaunchUs;
+  const int64_t wgs = std::max<int64_t>(cdiv(d.M, t.bm) * cdiv(d.N, t.bn) * d.batch * ranges, 1);
+  const int64_t cus = std::max(caps.num_cus, 1);
+  const int64_t slots = cus * c.per_cu;
+  const double mn = (double)d.M * (double)d.N * (double)d.batch;
+  double us = kFixedUs + mn * out_size(d.out_dtype) / kStoreBytesPerUs;
+  for (int64_t left = wgs; left > 0; left -= slots) {
+    const int64_t w = std::min(left, slots);
+    double trip;
+    if (w > cus)
+      trip = c.trip_shared;
+    else if (c.power_scaled)
+      trip = c.trip_alone + (c.trip_shared - c.trip_alone) * (double)w / (double)cus;
+    else
+      trip = c.trip_alone;
+    us += (double)tps * trip;
   }
+  if (ranges > 1) us += (2.0 * ranges * mn * 4.0 + mn * out_size(d.out_dtype)) / kReduceBytesPerUs + kLaunchUs;
   return us;
 }
 
@@ -138,9 +155,11 @@ constexpr int64_t kMinTripsPerSplit = 8;
 // Choose a tile (and, where allowed, a split) for the problem: short-K
 // products whose N is a multiple of 96 take the 256 x 96 tile (few trips,
 // many workgroups to stream A and C; measured faster than one 128 x 288 tile
-// per row block); the rest take the general tile and split with the lowest
-// estimated time.  The deeper-ring tiles (6, 7) are selected by id.  FP8
-// operands choose among their own tiles (8, 9, 10).
+// per row block); the rest take the tile and split with the lowest
+// estimated time among 256 x 256, 128 x 128, 64 x 64 and the 128 x 128
+// ring of half-depth slots (which wins mid sizes such as 2048^3).  Tiles
+// 4-6 otherwise run only when asked for by id.  FP8 operands choose among
+// their own tiles (8, 9, 10).
 void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, int* tile, int64_t* splits) {
   *splits = 1;
   const bool fp8 = d.in_dtype == GEMM_FP8;
@@ -152,8 +171,15 @@ void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, in
     return;
   }
   double best_t = 1e300;
-  const int lo = d.tile ? d.tile : (fp8 ? 8 : 1), hi = d.tile ? d.tile : (fp8 ? 10 : 3);
-  for (int id = lo; id <= hi; ++id) {
+  static const int kGeneral16[] = {1, 2, 3, 7}, kGeneral8[] = {8, 9, 10};
+  const int* ids = fp8 ? kGeneral8 : kGeneral16;
+  int n_ids = fp8 ? 3 : 4;
+  if (d.tile) {
+    ids = &d.tile;
+    n_ids = 1;
+  }
+  for (int k = 0; k < n_ids; ++k) {
+    const int id = ids[k];
     const int64_t trips = cdiv(d.K, tile_desc(id).bk);
     for (int64_t sp = 1; sp <= kMaxSplits; sp *= 2) {
       if (sp > 1 && (!may_split || trips / sp < kMinTripsPerSplit)) break;
