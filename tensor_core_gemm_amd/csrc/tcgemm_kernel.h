@@ -216,27 +216,34 @@ struct TilePos {
 };
 
 __device__ __forceinline__ TilePos tile_of(const KArgs& a) {
-  int64_t wg = blockIdx.x;
+  // The planner keeps workgroups x lanes below 2^32, so every count here
+  // fits 32 bits: 32-bit divisions are a fraction of the scalar code of
+  // 64-bit ones, and this runs before the first copy can issue.
+  uint32_t wg = blockIdx.x;
   // Workgroups are dealt to the 8 XCDs round-robin; renumber so that the
   // workgroups on one XCD take consecutive tiles (which share A rows and B
   // columns in that XCD's L2).
   if (a.xcd_remap) {
-    const int64_t q = a.workgroups / 8;
+    const uint32_t q = (uint32_t)a.workgroups / 8;
     if (wg < 8 * q) wg = (wg % 8) * q + wg / 8;
   }
-  const int64_t per_batch = a.tiles_m * a.tiles_n;
-  const int64_t per_split = per_batch * a.batch;
+  const uint32_t tiles_m = (uint32_t)a.tiles_m, tiles_n = (uint32_t)a.tiles_n;
+  const uint32_t per_batch = tiles_m * tiles_n;
+  const uint32_t per_split = per_batch * (uint32_t)a.batch;
   TilePos p;
-  p.split = wg / per_split;
-  wg -= p.split * per_split;
-  p.b = wg / per_batch;
-  const int64_t t = wg - p.b * per_batch;
+  const uint32_t split = wg / per_split;
+  wg -= split * per_split;
+  const uint32_t b = wg / per_batch;
+  const uint32_t t = wg - b * per_batch;
   // grouped order: group_m tile rows at a time, column-major inside a group
-  const int64_t in_group = (int64_t)a.group_m * a.tiles_n;
-  const int64_t g = t / in_group;
-  const int64_t first = g * a.group_m;
-  const int64_t gsize = (a.tiles_m - first) < a.group_m ? (a.tiles_m - first) : a.group_m;
-  const int64_t r = t - g * in_group;
+  const uint32_t group_m = (uint32_t)a.group_m;
+  const uint32_t in_group = group_m * tiles_n;
+  const uint32_t g = t / in_group;
+  const uint32_t first = g * group_m;
+  const uint32_t gsize = (tiles_m - first) < group_m ? (tiles_m - first) : group_m;
+  const uint32_t r = t - g * in_group;
+  p.split = split;
+  p.b = b;
   p.tm = first + r % gsize;
   p.tn = r / gsize;
   return p;
