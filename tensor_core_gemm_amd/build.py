@@ -28,6 +28,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-packed-fp32-ops"]
 
 
+# Per-source flags.  The persistent short-K kernel keeps its accumulators in
+# ordinary VGPRs (MFMAs in their VGPR form): its epilogue then reads them
+# directly instead of copying every value out of the accumulation registers
+# first, which made the epilogue the longest step of each block.
+EXTRA = {"tcgemm_shortk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
@@ -39,7 +46,8 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     for src in sources():
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *COMMON, *(extra or []), "-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), *(extra or []), "-x", "hip", "-c", src,
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,

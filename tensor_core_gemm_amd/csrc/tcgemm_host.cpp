@@ -148,6 +148,18 @@ double estimate_us(const gemm_desc& d, const gemm_device_caps& caps, int id, int
   return us;
 }
 
+// Problems the persistent short-K kernel (tile 11) takes: 16-bit operands,
+// one batch item, 0 < K <= 96 and 0 < N <= 288 with 16-byte rows (K and N
+// multiples of 8), no bias, the activation none or relu, staged, no split
+// and no cap on the stage count.
+bool shortk_fits(const gemm_desc& d) {
+  using namespace tcg::shortk;
+  return d.in_dtype != GEMM_FP8 && d.batch == 1 && d.M > 0 && d.K > 0 && d.K <= kKMax && d.K % 8 == 0 &&
+         d.N > 0 && d.N <= kNMax && d.N % 8 == 0 && d.split_k <= 1 &&
+         (d.epilogue == GEMM_EPI_NONE || d.epilogue == GEMM_EPI_RELU) &&
+         !(d.flags & (GEMM_FLAG_BIAS | GEMM_FLAG_UNSTAGED | GEMM_FLAG_FORCE_STAGES_1 | GEMM_FLAG_FORCE_STAGES_2));
+}
+
 // Split counts the planner considers: powers of two while every range keeps
 // at least kMinTripsPerSplit trips.
 constexpr int64_t kMinTripsPerSplit = 8;
@@ -166,6 +178,9 @@ void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, in
   if (d.tile) {
     *tile = d.tile;
     if (!may_split) return;
+  } else if (shortk_fits(d) && d.M >= (int64_t)tcg::shortk::kBM * caps.num_cus) {
+    *tile = 11;
+    return;
   } else if (!fp8 && d.K <= 128 && d.N > 0 && d.N % 96 == 0) {
     *tile = 4;
     return;
@@ -305,6 +320,53 @@ extern "C" int gemm_stage_depth(const gemm_device_caps* caps, int64_t used, cons
   return 0;
 }
 
+// The plan of the persistent short-K kernel.  It reports the 32-deep trips
+// of the MFMA sequence it shares with tile 5 (bk = 32), so that a run whose
+// pointers are not 16-byte aligned can take tile 5's kernel instead.
+static int plan_shortk(const gemm_desc& d, const gemm_device_caps& caps, gemm_plan_t* out) {
+  using namespace tcg::shortk;
+  if (!shortk_fits(d)) return GEMM_E_ARG;
+  if (caps.lds_bytes < kLdsBytes) return GEMM_E_DEVICE;
+  const int64_t blocks = cdiv(d.M, kBM);
+  if (blocks >= ((int64_t)1 << 30)) return GEMM_E_SIZE;
+  Plan* p = new (std::nothrow) Plan();
+  if (!p) return GEMM_E_NOMEM;
+  p->magic = kPlanMagic;
+  p->d = d;
+  gemm_plan_info& in = p->info;
+  in.tile_id = 11;
+  in.bm = kBM;
+  in.bn = kNMax;
+  in.bk = 32;
+  in.waves = 4;
+  in.stages = kSlots;
+  in.lds_bytes = kLdsBytes;
+  in.vec16 = 1;
+  in.tiles_m = blocks;
+  in.tiles_n = 1;
+  in.workgroups = std::min<int64_t>(blocks, std::max(caps.num_cus, 1));
+  in.trips = cdiv(d.K, 32);
+  in.mfma_per_run = blocks * 4 * kFN * 2 * in.trips;
+  in.mfma_m = tcg::kMfmaM;
+  in.mfma_n = tcg::kMfmaN;
+  in.mfma_k = tcg::kMfmaK;
+  in.split_k = 1;
+  in.trips_per_split = in.trips;
+  in.workspace_bytes = 0;
+  p->group_m = (int32_t)std::min<int64_t>(4, blocks);
+  p->xcd_remap = 0;
+  std::snprintf(p->text, sizeof(p->text),
+                "tile 11 (persistent, 128-row blocks, N <= %d, K <= %d, 4 waves), B image in LDS, %d A slots, "
+                "LDS %d B, grid %lld over %lld blocks, trips %lld, mfma 32x32x16 %s, %lld MFMAs, epilogue %s",
+                kNMax, kKMax, kSlots, kLdsBytes, (long long)in.workgroups, (long long)blocks, (long long)in.trips,
+                d.in_dtype == GEMM_BF16 ? "bf16" : "f16", (long long)in.mfma_per_run,
+                d.epilogue == GEMM_EPI_RELU ? "relu" : "none");
+  if (log_enabled()) std::fprintf(stderr, "[tcgemm] plan %lldx%lldx%lld: %s\n", (long long)d.M,
+                                  (long long)d.N, (long long)d.K, p->text);
+  *out = reinterpret_cast<gemm_plan_t>(p);
+  return GEMM_OK;
+}
+
 extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps* caps, gemm_plan_t* out) {
   if (!out) return GEMM_E_ARG;
   *out = nullptr;
@@ -326,6 +388,7 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
     choose(d, *caps, (d.flags & GEMM_FLAG_SPLIT_K) != 0, &id, &want_splits);
   }
   const auto& t = tile_desc(id);
+  if (t.persistent) return plan_shortk(d, *caps, out);
 
   const int64_t tiles[2] = {(int64_t)t.bm * t.bk * t.esize, (int64_t)t.bk * t.bn * t.esize};
   int stages = gemm_stage_depth(caps, 0, tiles, 2, (d.flags & GEMM_FLAG_UNSTAGED) ? 0 : 1);
@@ -541,6 +604,17 @@ extern "C" int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void*
   // The general epilogue's kernels only where the GEMM finishes C itself
   // with a bias or a transcendental activation.
   const bool gen = in.split_k == 1 && (bias || (d.epilogue != GEMM_EPI_NONE && d.epilogue != GEMM_EPI_RELU));
+  if (in.tile_id == 11) {
+    if (vec16 && a.vec_store16 && (c0 % 16u) == 0) {
+      e = tcg::launch_t11(bf16, a, s);
+    } else {
+      // Rows not 16-byte aligned: tile 5's kernel, the same MFMA sequence
+      // (identical bits), with element copies or element stores.
+      a.workgroups = in.tiles_m;
+      a.group_m = (int32_t)std::min<int64_t>(4, in.tiles_m);
+      e = tcg::launch_t5(2, vec16, bf16, a, s);
+    }
+  }
   switch (in.tile_id) {
     case 1: e = (gen ? tcg::launch_t1_gen : tcg::launch_t1)(in.stages, vec16, bf16, a, s); break;
     case 2: e = (gen ? tcg::launch_t2_gen : tcg::launch_t2)(in.stages, vec16, bf16, a, s); break;

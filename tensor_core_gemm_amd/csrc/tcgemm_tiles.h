@@ -21,6 +21,7 @@ struct TileDesc {
   int max_stages;  // deepest LDS ring the kernel is built for
   int min_waves;   // waves per SIMD the register budget must allow (workgroups per CU)
   int esize;       // operand element bytes: 2 (fp16, bf16) or 1 (FP8 E4M3)
+  int persistent;  // 1: the persistent short-K kernel (bk, bn: the largest K and N it takes)
 };
 
 // id 0 is "planner's choice" in the ABI; real ids start at 1.
@@ -35,6 +36,7 @@ constexpr TileDesc kTiles[] = {
     {8, 256, 256, 128, 2, 2, 2, 1, 1},  // FP8, wave 128 x 128
     {9, 128, 128, 128, 2, 2, 2, 2, 1},  // FP8, wave 64 x 64
     {10, 64, 64, 128, 2, 2, 2, 2, 1},   // FP8, wave 32 x 32
+    {11, 128, 288, 96, 4, 1, 3, 1, 2, 1},  // persistent short K: wave 32 x 288, B resident
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -98,6 +100,31 @@ struct Tile {
   static_assert(BK % MK == 0 && (BK * ES) % 16 == 0, "BK must be whole k-steps and chunks");
   static_assert((BN * ES) % 16 == 0, "BN must be whole chunks");
 };
+
+// The persistent short-K kernel (tile 11): one workgroup per CU loops over
+// 128-row blocks of A and C.  B (K <= 96 rows, N <= 288 columns) is copied
+// once into an LDS image that stays for the whole launch (rows 576 bytes
+// apart, so the four rows a transposing fragment read touches fall on four
+// different 64-byte bank ranges).  A blocks pass through a ring of three
+// LDS slots (rows of 12 16-byte chunks, the chunk index XORed with
+// (row / 4) mod 4 so that the 16 rows a fragment read touches fall on 16
+// different bank groups).  Each wave's outputs pass through its own LDS
+// band of 32 rows x 96 columns (16-bit outputs) or 32 x 32 (fp32).
+namespace shortk {
+constexpr int kBM = 128, kFN = 9, kNMax = 32 * kFN, kKMax = 96, kKS = kKMax / 16;
+constexpr int kSlots = 3;
+constexpr int kCprA = kKMax * 2 / 16;              // chunks per A row in LDS
+constexpr int kSlotA = kBM * kCprA * 16;           // one A slot
+constexpr int kCprB = kNMax * 2 / 16;              // chunks per B row in LDS
+constexpr int kBBytes = kKMax * kCprB * 16;        // the B image
+constexpr int kBandWave = 32 * (96 * 2 + 16);      // one wave's band (also holds 32 x 32 fp32)
+constexpr int kLdsBytes = kBBytes + 4 * kBandWave + kSlots * kSlotA;
+constexpr int kCopiesA = kBM * kCprA / 256;        // copy instructions per wave per A block
+constexpr int kCopiesB = (kKMax * kCprB + 63) / 64;  // wave copy instructions for B
+static_assert(kBM * kCprA % 256 == 0, "A blocks are whole copy rounds");
+static_assert(32 * (32 * 4 + 16) <= kBandWave, "an fp32 band fits");
+static_assert(kLdsBytes <= 163840, "fits gfx950's LDS");
+}  // namespace shortk
 
 // Largest power of two dividing n, minus one: the XOR mask that keeps a
 // swizzled chunk index inside its row when a row has n chunks.

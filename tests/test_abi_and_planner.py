@@ -94,9 +94,52 @@ def test_stage_fallbacks_follow_lds_budget():
     assert p.info().stages == 0 and p.info().lds_bytes == 4 * 32 * (64 * 4 + 16)
 
 
-def test_short_k_token_projection_takes_wide_tile():
+def test_short_k_token_projection_takes_the_persistent_tile():
+    """Many rows, K <= 96 and N <= 288 (multiples of 8), at least one 128-row
+    block per CU: the persistent short-K kernel (tile 11), one workgroup per
+    CU (grid = CUs) over ceil(M / 128) blocks, three A slots."""
     i = plan(129600, 288, 96, F16, F16, EPI_NONE).info()
-    assert (i.bm, i.bn, i.bk) == (256, 96, 32) and i.tiles_n == 3 and i.trips == 3
+    assert (i.tile_id, i.bm, i.bn, i.bk, i.stages) == (11, 128, 288, 32, 3)
+    assert (i.tiles_m, i.tiles_n, i.workgroups, i.trips) == (1013, 1, 256, 3)
+    assert i.lds_bytes == 96 * 576 + 4 * 32 * 208 + 3 * 128 * 192
+    assert i.mfma_per_run == 1013 * 4 * 9 * 6
+    assert plan(129600, 288, 96, F16, F16, EPI_RELU).info().tile_id == 11
+    assert plan(65536, 192, 64, BF16, F32, EPI_NONE).info().tile_id == 11
+    assert "persistent" in plan(129600, 288, 96, F16, F16, EPI_NONE).describe()
+
+
+def test_short_k_falls_back_to_the_wide_tile():
+    """Where the persistent kernel does not apply, short-K products whose N is
+    a multiple of 96 take the 256 x 96 tile."""
+    def tile(M=129600, N=288, K=96, **kw):
+        return plan(M, N, K, F16, F16, EPI_NONE, **kw).info()
+    i = tile(caps=tcg.make_caps(num_cus=1024))  # fewer blocks than CUs
+    assert (i.tile_id, i.bm, i.bn, i.bk, i.tiles_n, i.trips) == (4, 256, 96, 32, 3, 3)
+    assert tile(K=128).tile_id == 4
+    assert tile(N=384).tile_id == 4
+    assert tile(flags=tcg.FLAG_BIAS).tile_id == 4
+    assert tile(flags=tcg.FLAG_UNSTAGED).tile_id == 4
+    assert tile(flags=tcg.FLAG_FORCE_STAGES_1).tile_id == 4
+    assert tile(flags=tcg.FLAG_FORCE_STAGES_2).tile_id == 4
+    assert tile(batch=2, sa=129600 * 96, sb=96 * 288, sc=129600 * 288).tile_id == 4
+    assert plan(129600, 288, 96, F16, F16, 2).info().tile_id == 4  # gelu
+
+
+def test_persistent_tile_rejects_what_it_does_not_take():
+    ok = dict(M=5000, N=288, K=96, in_dtype=F16, out_dtype=F16, epi=EPI_NONE, tile=11)
+    assert plan(**ok).info().tile_id == 11
+    for kw in (dict(K=104), dict(N=296), dict(K=92), dict(N=100), dict(M=0), dict(K=0),
+               dict(batch=2, sa=5000 * 96, sb=96 * 288, sc=5000 * 288), dict(flags=tcg.FLAG_BIAS), dict(flags=tcg.FLAG_UNSTAGED),
+               dict(flags=tcg.FLAG_FORCE_STAGES_1), dict(flags=tcg.FLAG_FORCE_STAGES_2),
+               dict(split_k=2), dict(epi=2), dict(in_dtype=tcg.FP8)):
+        with pytest.raises(tcg.GemmError) as e:
+            plan(**{**ok, **kw})
+        assert e.value.code == tcg.GEMM_E_ARG, kw
+    with pytest.raises(tcg.GemmError) as e:
+        plan(**ok, caps=tcg.make_caps(lds_bytes=128 * 1024))
+    assert e.value.code == tcg.GEMM_E_DEVICE
+    # fewer blocks than CUs: one workgroup per block
+    assert plan(**{**ok, "M": 1000}).info().workgroups == 8
 
 
 def test_ragged_and_small_shapes_fill_the_chip():
@@ -150,15 +193,19 @@ def test_degenerate_sizes_plan():
 FP8_TILES = (8, 9, 10)
 
 
+SHORT_K_TILES = (11,)
+
+
 def test_every_tile_id_plans():
     for t in range(1, tcg.gemm_tile_count() + 1):
         dt = tcg.FP8 if t in FP8_TILES else BF16
-        i = plan(1000, 1000, 1000, in_dtype=dt, tile=t).info()
+        N, K = (288, 96) if t in SHORT_K_TILES else (1000, 1000)
+        i = plan(1000, N, K, in_dtype=dt, tile=t).info()
         assert i.tile_id == t and i.stages >= 2
         assert i.lds_bytes <= 163840
         # a tile is built for one operand width
         with pytest.raises(tcg.GemmError) as e:
-            plan(1000, 1000, 1000, in_dtype=BF16 if t in FP8_TILES else tcg.FP8, tile=t)
+            plan(1000, N, K, in_dtype=BF16 if t in FP8_TILES else tcg.FP8, tile=t)
         assert e.value.code == tcg.GEMM_E_ARG
 
 

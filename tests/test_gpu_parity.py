@@ -73,12 +73,13 @@ def test_full_size_sampled(tcg, name):
     check_sampled(w, A, B, C)
 
 
-@pytest.mark.parametrize("tile", [4, 5])
+@pytest.mark.parametrize("tile", [4, 5, 11])
 def test_swin_full_size_every_output(tcg, tile):
-    """The Swin projection at full size on both short-K tiles, every output
-    checked: the last tile row is ragged (129600 = 506 x 256 + 64) and the B
-    copies are partial rounds, so the wait for the first chunk must count
-    the copies of the waves that issue fewer."""
+    """The Swin projection at full size on the three short-K tiles, every
+    output checked: the last tile row is ragged (129600 = 506 x 256 + 64) and
+    the B copies are partial rounds, so the wait for the first chunk must
+    count the copies of the waves that issue fewer; the persistent tile runs
+    four blocks per workgroup through its three-slot ring."""
     w = W["swin_proj_fp16"]
     A, B = gw.make_inputs(w)
     C, _, p = run(tcg, A, B, w, tile=tile)
@@ -98,12 +99,18 @@ def test_full_size_runs_are_bitwise_stable(tcg, name):
         assert np.array_equal(as_bits(run(tcg, A, B, w, plan=p)[0]), first)
 
 
+# The persistent short-K tile runs the MFMA sequence of the 128 x 288 x 32
+# tile (one stage, unstaged and two-stage kernels of its own are not built):
+# its one-stage and unstaged references are that tile's.
+SAME_SEQUENCE = {11: 5}
+
+
 @pytest.mark.parametrize("name", list(W))
 def test_staged_equals_unstaged_bitwise(tcg, name):
     w = W[name]
     A, B = gw.make_inputs(w)
     Cs, _, ps = run(tcg, A, B, w)
-    tile = ps.info().tile_id
+    tile = SAME_SEQUENCE.get(ps.info().tile_id, ps.info().tile_id)
     Cu, _, pu = run(tcg, A, B, w, flags=tcg.FLAG_UNSTAGED, tile=tile)
     assert pu.info().stages == 0 and ps.info().stages > 0
     assert np.array_equal(as_bits(Cs), as_bits(Cu))
@@ -114,7 +121,8 @@ def test_one_stage_equals_two_stages_bitwise(tcg, name):
     w = W[name]
     A, B = gw.make_inputs(w)
     C2, _, p2 = run(tcg, A, B, w)
-    C1, _, p1 = run(tcg, A, B, w, flags=tcg.FLAG_FORCE_STAGES_1, tile=p2.info().tile_id)
+    tile = SAME_SEQUENCE.get(p2.info().tile_id, p2.info().tile_id)
+    C1, _, p1 = run(tcg, A, B, w, flags=tcg.FLAG_FORCE_STAGES_1, tile=tile)
     assert p2.info().stages >= 2 and p1.info().stages == 1
     assert np.array_equal(as_bits(C1), as_bits(C2))
 
