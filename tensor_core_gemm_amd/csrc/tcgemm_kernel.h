@@ -312,7 +312,37 @@ __device__ __forceinline__ OutRef out_ref(const KArgs& a, const TilePos& tp) {
 // loads, branches and transcendental functions would be copied into each of
 // a wave's 64 groups.
 
+// The rounded epilogue's activation without a branch: fmax(floor, v) with
+// floor = +0 is relu (a NaN v gives +0, as Tile.relu requires; -0 gives
+// +0), and with floor = a quiet NaN it returns v unchanged (maxNum returns
+// the other operand when one is a NaN, and NaN when both are).  A branch
+// between two epilogues here made the compiler read every accumulator before
+// it and spill.  (This stays a compiler max, not a hand-written v_max: the
+// compiler must see the read of an MFMA result to wait for it.)
+__device__ __forceinline__ float max_floor(float floor, float v) { return __builtin_fmaxf(floor, v); }
+__device__ __forceinline__ float act_floor(int act) {
+  return act == kActRelu ? 0.0f : __builtin_bit_cast(float, 0x7fc00000u);
+}
+
+// Two fp32 values rounded to nearest-even in one instruction (gfx950's
+// packed conversions), the first in the low half.
+template <int OUT>
+__device__ __forceinline__ uint32_t round2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  if constexpr (OUT == kOutBF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
 // Rounded band (no bias; activation none or relu), OUT the output type.
+// Whole 16-byte chunks of C (o.vec16) leave as buffer stores at 32-bit
+// offsets from the band's first element: rows past M lie past the
+// resource's end and columns past N get an offset past it, so the buffer
+// unit drops both and no lane branches.  Otherwise each chunk is stored
+// element by element.
 template <class T, int OUT, bool NT>
 __device__ __forceinline__ void store_rounded(const OutRef& o, const f32x16 (&acc)[T::FM][T::FN],
                                               int64_t m0, int64_t n0, int lane, int w, lds_char* smem) {
@@ -323,7 +353,9 @@ __device__ __forceinline__ void store_rounded(const OutRef& o, const f32x16 (&ac
   lds_char* band = smem + w * T::EPI_WAVE_BYTES;
   constexpr int cpr = EPW * osz / 16;  // 16-byte chunks per band row
   constexpr int per_elem = 16 / osz;   // elements per chunk
-  const bool relu = o.act == kActRelu;
+  const bool buffered = o.vec16 && N * osz * 32 < (int64_t)0x7fffffff;
+  constexpr int aux = NT ? 2 : 0;  // the non-temporal cache policy bit
+  const float floor = act_floor(o.act);  // uniform: one SGPR
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
 #pragma unroll
@@ -342,14 +374,13 @@ __device__ __forceinline__ void store_rounded(const OutRef& o, const f32x16 (&ac
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float v = acc[i][j][4 * g + q];
-            y[q] = relu ? (v > 0.0f ? v : 0.0f) : v;  // Tile.relu: NaN and -0 give +0
+            y[q] = max_floor(floor, v);  // relu or none
           }
-          if (osz == 4) {
+          if constexpr (osz == 4) {
             *(__attribute__((address_space(3))) f32x4*)(band + row * pitch + col * 4) = f32x4{y[0], y[1], y[2], y[3]};
           } else {
-            const uint32_t lo = pack2(to_out16(y[0], OUT), to_out16(y[1], OUT));
-            const uint32_t hi = pack2(to_out16(y[2], OUT), to_out16(y[3], OUT));
-            *(__attribute__((address_space(3))) u32x2*)(band + row * pitch + col * 2) = u32x2{lo, hi};
+            *(__attribute__((address_space(3))) u32x2*)(band + row * pitch + col * 2) =
+                u32x2{round2<OUT>(y[0], y[1]), round2<OUT>(y[2], y[3])};
           }
         }
       }
@@ -358,18 +389,28 @@ __device__ __forceinline__ void store_rounded(const OutRef& o, const f32x16 (&ac
       const int64_t mb = m0 + 32 * i;
       const int64_t nb = n0 + EPW * jb;
       constexpr int chunks = 32 * cpr;
+      if (buffered) {
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(o.C + (mb * N + nb) * osz, ((M - mb) * N - nb) * osz);
+        const int ncols = (int)(N - nb < EPW ? N - nb : EPW);  // columns of this band inside C
 #pragma unroll
-      for (int idx = lane; idx < chunks; idx += 64) {
-        const int r = idx / cpr;
-        const int ch = idx - r * cpr;
-        const u32x4 v = *(const lds_u32x4*)(band + r * pitch + ch * 16);
-        const int64_t m = mb + r;
-        const int64_t n = nb + (int64_t)ch * per_elem;
-        if (m >= M || n >= N) continue;
-        char* dst = o.C + (m * N + n) * osz;
-        if (o.vec16 && n + per_elem <= N) {
-          store_vec<NT>(dst, v);
-        } else {
+        for (int idx = lane; idx < chunks; idx += 64) {
+          const int r = idx / cpr;
+          const int ch = idx - r * cpr;
+          const u32x4 v = *(const lds_u32x4*)(band + r * pitch + ch * 16);
+          const int c = ch * per_elem;
+          const uint32_t off = c < ncols ? (uint32_t)((r * (int)N + c) * osz) : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, aux);
+        }
+      } else {
+#pragma unroll
+        for (int idx = lane; idx < chunks; idx += 64) {
+          const int r = idx / cpr;
+          const int ch = idx - r * cpr;
+          const u32x4 v = *(const lds_u32x4*)(band + r * pitch + ch * 16);
+          const int64_t m = mb + r;
+          const int64_t n = nb + (int64_t)ch * per_elem;
+          if (m >= M || n >= N) continue;
+          char* dst = o.C + (m * N + n) * osz;
           const int cnt = (int)((N - n) < per_elem ? (N - n) : per_elem);
           if (osz == 4) {
             for (int q = 0; q < cnt; ++q) ((uint32_t*)dst)[q] = v[q];
