@@ -201,8 +201,17 @@ def main():
 
     flops = w.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    peak = PEAK_MFMA_TFLOPS[w.in_dtype]
+    peak_mfma = PEAK_MFMA_TFLOPS[w.in_dtype]
+    # The roofline that bounds the workload: MFMA where its arithmetic
+    # intensity (flops per algorithmic byte) is above the ridge point
+    # (peak flops / HBM bandwidth), HBM below it.
+    hbm_bound = w.flops / w.algorithmic_bytes < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved = w.algorithmic_bytes / (avg_launch_ms * 1e-3) / 1e9
+        peak, bound, unit = PEAK_HBM_GBS, "hbm", "GB/s"
+    else:
+        achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+        peak, bound, unit = peak_mfma, "mfma", "TFLOP/s"
 
     # quick sanity check of the timed output against the oracle (64 samples)
     import numpy as np
@@ -241,15 +250,15 @@ def main():
             "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
             "in": gw.DTYPE_NAME[w.in_dtype], "out": gw.DTYPE_NAME[w.out_dtype],
             "epilogue": "relu" if w.epilogue else "none", "accumulate": "f32",
-            "plan": plan.describe(), "pct_of_peak": round(100 * value / peak, 2),
+            "plan": plan.describe(), "pct_of_peak": round(100 * value / peak_mfma, 2),
             "device": caps.arch.decode(), "cus": caps.num_cus, "clock_mhz": caps.clock_khz // 1000,
             "sample_max_rel_err": sample_err,
         },
         "roofline": {
-            "bound": "mfma",
+            "bound": bound,
             "achieved": round(achieved, 2),
             "peak": peak,
-            "unit": "TFLOP/s",
+            "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_avg_ms": round(avg_launch_ms, 5),
@@ -318,14 +327,16 @@ def torch_matmul_time(w, io, warmup, steps, stream):
 
 
 def kernel_source_sha() -> str:
-    """Hash of the GEMM kernel's device sources (headers and kernel
-    instantiations; not the host planner, the probes or the reduction), so
-    that counter data taken from another kernel is not reported."""
+    """Hash of the GEMM kernels' device sources (headers, kernel
+    instantiations and the persistent short-K kernel; not the host planner,
+    the probes or the reduction), so that counter data taken from another
+    kernel is not reported."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_core_gemm_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
-        if fn.endswith(".h") or (fn.startswith("tcgemm_inst_") and fn.endswith(".hip")):
+        if fn.endswith(".h") or (fn.startswith("tcgemm_inst_") and fn.endswith(".hip")) or \
+                fn == "tcgemm_shortk.hip":
             with open(os.path.join(csrc, fn), "rb") as f:
                 h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]

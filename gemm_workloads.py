@@ -76,8 +76,9 @@ class Workload:
     @property
     def algorithmic_bytes(self) -> int:
         """A and B read once, C written once."""
+        in_size = 1 if self.in_dtype == FP8 else 2
         out_size = 4 if self.out_dtype == F32 else 2
-        return self.batch * (2 * (self.M * self.K + self.K * self.N) + out_size * self.M * self.N)
+        return self.batch * (in_size * (self.M * self.K + self.K * self.N) + out_size * self.M * self.N)
 
     def sigma_out(self) -> float:
         """Standard deviation of one output before the epilogue: sqrt(K) sA sB."""
