@@ -28,14 +28,14 @@ struct TileDesc {
 constexpr TileDesc kTiles[] = {
     {1, 256, 256, 64, 2, 2, 2, 1, 2},   // wave 128 x 128: large MFMA-bound products
     {2, 128, 128, 64, 2, 2, 2, 2, 2},   // wave 64 x 64: mid sizes / more workgroups
-    {3, 64, 64, 64, 2, 2, 2, 2, 2},     // wave 32 x 32: small and ragged products
+    {3, 64, 64, 64, 2, 2, 3, 2, 2},     // wave 32 x 32: small and ragged products, up to 3 slots
     {4, 256, 96, 32, 4, 1, 2, 2, 2},    // wave 64 x 96: short-K, N a multiple of 96
     {5, 128, 288, 32, 4, 1, 2, 1, 2},   // wave 32 x 288: short-K, N = 288 in one tile
     {6, 256, 256, 32, 2, 2, 4, 1, 2},   // wave 128 x 128, half-depth slots: up to 4 in flight
     {7, 128, 128, 32, 2, 2, 4, 2, 2},   // wave 64 x 64, half-depth slots: up to 4 in flight
     {8, 256, 256, 128, 2, 2, 2, 1, 1},  // FP8, wave 128 x 128
     {9, 128, 128, 128, 2, 2, 2, 2, 1},  // FP8, wave 64 x 64
-    {10, 64, 64, 128, 2, 2, 2, 2, 1},   // FP8, wave 32 x 32
+    {10, 64, 64, 128, 2, 2, 3, 2, 1},   // FP8, wave 32 x 32, up to 3 slots
     {11, 128, 288, 96, 4, 1, 3, 1, 2, 1},  // persistent short K: wave 32 x 288, B resident
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);

@@ -151,6 +151,27 @@ def test_ring_depths_give_the_same_bits(tcg, tile):
         del desc
 
 
+@pytest.mark.parametrize("tile,in_dtype", [(3, F16), (3, BF16), (10, gw.FP8)])
+def test_small_tile_rings_give_the_same_bits(tcg, tile, in_dtype):
+    """The 64 x 64 tiles keep up to three chunks in flight: rings of 3 and 2
+    slots, one stage and no staging give the same bits (ragged edges, odd
+    and even trip counts, a K tail inside the last chunk)."""
+    for M, N, K in ((1000, 1000, 1000), (130, 70, 448), (64, 64, 136), (300, 200, 4000)):
+        w = gw.custom(M, N, K, in_dtype, F32, EPI_RELU, gw.NORMAL, seed=K + tile)
+        A, B = gw.make_inputs(w)
+        ref = None
+        for lds, flags, want in ((163840, 0, 3), (163840, tcg.FLAG_FORCE_STAGES_2, 2),
+                                 (163840, tcg.FLAG_FORCE_STAGES_1, 1), (163840, tcg.FLAG_UNSTAGED, 0)):
+            d = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, flags, tile=tile)
+            p = tcg.gemm_plan_for_caps(d, tcg.make_caps(lds_bytes=lds))
+            assert p.info().stages == want
+            C = run(tcg, A, B, w, plan=p)[0]
+            if ref is None:
+                ref = as_bits(C)
+                check_against_oracle(w, A, B, C)
+            assert np.array_equal(as_bits(C), ref), (M, N, K, want)
+
+
 def test_repeat_runs_identical(tcg):
     w = W["ragged_fp16_1000"]
     A, B = gw.make_inputs(w)
@@ -196,7 +217,7 @@ def test_every_tile_gives_the_exact_integer_result(tcg, tile):
 # each chunk's copies between two trips; the last trips issue whole chunks
 # and finish a split one.  K = BK * trips - 8 leaves a partial last chunk.
 TRIP_CASES = [(tile, trips, flags) for tile, flags in ((1, 0), (2, 0), (3, 0), (6, 0), (7, 0),
-                                                       (6, "stages2"), (7, "stages2"))
+                                                       (3, "stages2"), (6, "stages2"), (7, "stages2"))
               for trips in range(1, 10)]
 
 
