@@ -118,10 +118,17 @@ enum {
 /* The problem.  M, N >= 0, K >= 0 (K == 0 gives C = epilogue(+0));
  * batch >= 1; with batch > 1, stride_a >= M*K, stride_b >= K*N and
  * stride_c >= M*N.  `tile` selects a tile configuration by id (1 ..
- * gemm_tile_count()), or 0 for the planner's choice; tiles 1-7 take 16-bit
- * operands and tiles 8-10 FP8 operands (another gives GEMM_E_ARG).  `split_k` cuts K into
- * that many ranges (1 .. 256; fewer if K has fewer trips), or 0 for one
- * range unless GEMM_FLAG_SPLIT_K lets the planner choose. */
+ * gemm_tile_count()), or 0 for the planner's choice; tiles 1-7 and 11 take
+ * 16-bit operands and tiles 8-10 FP8 operands (another gives GEMM_E_ARG).
+ * Tile 11 is the persistent short-K kernel (one workgroup per CU looping
+ * over 128-row blocks, B held in LDS for the whole launch); it takes only
+ * batch 1, 0 < K <= 96 and 0 < N <= 288 with K and N multiples of 8, no
+ * bias, GEMM_EPI_NONE or GEMM_EPI_RELU, no split and none of the stage
+ * flags (GEMM_E_ARG otherwise), and it gives the same bits as tile 5.  The
+ * planner picks it for such problems with at least one block per CU.
+ * `split_k` cuts K into that many ranges (1 .. 256; fewer if K has fewer
+ * trips), or 0 for one range unless GEMM_FLAG_SPLIT_K lets the planner
+ * choose. */
 typedef struct gemm_desc {
   int64_t M, N, K;
   int32_t in_dtype;  /* GEMM_F16, GEMM_BF16 or GEMM_FP8 (A and B) */
@@ -154,8 +161,10 @@ typedef struct gemm_plan_info {
   int32_t stages;           /* LDS slots in the ring (2..4), 1, or 0 (unstaged) */
   int32_t lds_bytes;        /* LDS the kernel declares                       */
   int32_t vec16;            /* 1: 16-byte copies; 0: element copies          */
-  int64_t tiles_m, tiles_n; /* output tiles along M and N                    */
-  int64_t workgroups;       /* tiles_m * tiles_n * batch * split_k           */
+  int64_t tiles_m, tiles_n; /* output tiles along M and N (tile 11: 128-row
+                               blocks and 1)                                 */
+  int64_t workgroups;       /* tiles_m * tiles_n * batch * split_k (tile 11:
+                               min(blocks, CUs), each looping over blocks)   */
   int64_t trips;            /* K-trips: ceil(K / bk)                         */
   int64_t mfma_per_run;     /* MFMA instructions one run issues              */
   int32_t mfma_m, mfma_n, mfma_k;
