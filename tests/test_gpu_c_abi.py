@@ -30,6 +30,9 @@ def raw(t):
     gw.custom(256, 256, 256, F16, F32, EPI_RELU, gw.INT4, seed=1, name="int_f16"),
     gw.custom(300, 200, 130, BF16, BF16, EPI_NONE, gw.NORMAL, seed=2, name="ragged_bf16"),
     gw.custom(130, 96, 256, FP8, F32, EPI_RELU, gw.NORMAL, seed=3, name="fp8"),
+    # enough rows for the persistent short-K tile (one 128-row block per CU or more)
+    gw.custom(40000, 288, 96, F16, F16, EPI_NONE, gw.NORMAL, seed=4, name="short_k_f16",
+              dist_b=gw.Dist("normal", 0.0, 96 ** -0.5)),
 ], ids=lambda w: w.name)
 def test_c_client_matches_the_oracle(w, tmp_path):
     if not torch.cuda.is_available():
@@ -46,6 +49,8 @@ def test_c_client_matches_the_oracle(w, tmp_path):
     print(r.stdout, r.stderr)
     assert r.returncode == 0, r.stderr
     assert "plan: tile" in r.stdout and r.stdout.strip().endswith("ok")
+    if w.name == "short_k_f16":
+        assert "plan: tile 11" in r.stdout
     odt = np.float32 if w.out_dtype == F32 else np.uint16
     C = np.frombuffer(pc.read_bytes(), odt).reshape(w.M, w.N)
     ref, Y = oracle.gemm(A, B, w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, want_y=True)
