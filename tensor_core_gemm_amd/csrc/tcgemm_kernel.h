@@ -86,12 +86,18 @@ template <int CPR>
 __device__ __forceinline__ int swz_a(int r) {
   return (r >> swz_a_shift<CPR>()) & swizzle_mask(CPR);
 }
-// B with 8-bit elements: a transposing 8-byte read of 32 lanes covers 8
-// rows and two adjacent chunks of each, so the XOR spreads 8 rows over 8
-// chunk pairs: 2(r mod 8).
+// B with 16-bit elements: a transposing 8-byte read of 32 lanes covers 4
+// rows and 4 adjacent chunks of each (64 bytes), so where a row has 16
+// chunks or more the XOR 4(r mod 4) gives the 4 rows 4 different 64-byte
+// bank ranges; narrower rows keep 2(r mod 4).  B with 8-bit elements: a
+// read of 32 lanes covers 8 rows and two adjacent chunks of each, so the
+// XOR spreads 8 rows over 8 chunk pairs: 2(r mod 8).
 template <int CPR, int ES>
 __device__ __forceinline__ int swz_b(int r) {
-  return ES == 2 ? ((2 * (r & 3)) & swizzle_mask(CPR)) : ((2 * (r & 7)) & swizzle_mask(CPR));
+  if constexpr (ES == 2)
+    return (swizzle_mask(CPR) >= 15 ? 4 * (r & 3) : 2 * (r & 3)) & swizzle_mask(CPR);
+  else
+    return (2 * (r & 7)) & swizzle_mask(CPR);
 }
 // Rows after which swz_b repeats.
 template <int ES>
