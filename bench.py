@@ -335,18 +335,24 @@ def torch_matmul_time(w, io, warmup, steps, stream):
 
 
 def kernel_source_sha() -> str:
-    """Hash of the GEMM kernels' device sources (headers, kernel
-    instantiations and the persistent short-K kernel; not the host planner,
-    the probes or the reduction), so that counter data taken from another
-    kernel is not reported."""
+    """Hash of the code (comments and layout removed) of the GEMM kernels'
+    device sources (headers, kernel instantiations and the persistent
+    short-K kernel; not the host planner, the probes or the reduction), so
+    that counter data taken from other kernel code is not reported."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_core_gemm_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
         if fn.endswith(".h") or (fn.startswith("tcgemm_inst_") and fn.endswith(".hip")) or \
                 fn == "tcgemm_shortk.hip":
-            with open(os.path.join(csrc, fn), "rb") as f:
-                h.update(fn.encode() + f.read())
+            with open(os.path.join(csrc, fn)) as f:
+                text = f.read()
+            # code only: comments and layout do not change what runs
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            text = " ".join(text.split())
+            h.update(fn.encode() + text.encode())
     return h.hexdigest()[:16]
 
 
