@@ -226,6 +226,17 @@ def test_fp8_plans():
     assert e.value.code == tcg.GEMM_E_DTYPE
 
 
+def test_short_k_keeps_two_slots():
+    """With 4 trips or fewer the ring tiles keep two slots; past that they
+    take as many as fit (3 for the 64 x 64 tiles, 4 for 6 and 7)."""
+    assert plan(256, 256, 256, F16, F32, tile=3).info().stages == 2   # 4 trips
+    assert plan(256, 256, 320, F16, F32, tile=3).info().stages == 3   # 5 trips
+    assert plan(256, 256, 512, in_dtype=tcg.FP8, tile=10).info().stages == 2
+    assert plan(256, 256, 1024, in_dtype=tcg.FP8, tile=10).info().stages == 3
+    assert plan(4096, 4096, 128, tile=6).info().stages == 2           # 4 trips of 32
+    assert plan(4096, 4096, 4096, tile=6).info().stages == 4
+
+
 def test_deep_ring_follows_lds_budget():
     """Half-depth tiles keep more chunks in flight where they fit (page
     "gizml:tile", Program.stages): 4 slots, then 3, capped at 2 on request."""

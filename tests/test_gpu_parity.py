@@ -136,13 +136,15 @@ def test_ring_depths_give_the_same_bits(tcg, tile):
         A, B = gw.make_inputs(w)
         desc = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, tile=tile)
         ref = None
-        slot = tcg.gemm_plan_for_caps(desc, tcg.make_caps()).info().lds_bytes // 4
+        deep = tcg.make_desc(w.M, w.N, 1000, w.in_dtype, w.out_dtype, w.epilogue, tile=tile)
+        slot = tcg.gemm_plan_for_caps(deep, tcg.make_caps()).info().lds_bytes // 4  # a 4-slot plan
         for lds, flags, want in ((163840, 0, 4), (slot * 7 // 2, 0, 3),
                                  (163840, tcg.FLAG_FORCE_STAGES_2, 2),
                                  (163840, tcg.FLAG_FORCE_STAGES_1, 1), (163840, tcg.FLAG_UNSTAGED, 0)):
             d = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, flags, tile=tile)
             p = tcg.gemm_plan_for_caps(d, tcg.make_caps(lds_bytes=lds))
-            assert p.info().stages == want
+            # 4 trips or fewer keep two slots
+            assert p.info().stages == (min(want, 2) if -(-K // 32) <= 4 else want)
             bits = as_bits(run(tcg, A, B, w, plan=p)[0])
             if ref is None:
                 ref = bits
@@ -156,7 +158,7 @@ def test_small_tile_rings_give_the_same_bits(tcg, tile, in_dtype):
     """The 64 x 64 tiles keep up to three chunks in flight: rings of 3 and 2
     slots, one stage and no staging give the same bits (ragged edges, odd
     and even trip counts, a K tail inside the last chunk)."""
-    for M, N, K in ((1000, 1000, 1000), (130, 70, 448), (64, 64, 136), (300, 200, 4000)):
+    for M, N, K in ((1000, 1000, 1000), (130, 70, 448), (64, 64, 328), (300, 200, 4000)):
         w = gw.custom(M, N, K, in_dtype, F32, EPI_RELU, gw.NORMAL, seed=K + tile)
         A, B = gw.make_inputs(w)
         ref = None
@@ -164,7 +166,9 @@ def test_small_tile_rings_give_the_same_bits(tcg, tile, in_dtype):
                                  (163840, tcg.FLAG_FORCE_STAGES_1, 1), (163840, tcg.FLAG_UNSTAGED, 0)):
             d = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, flags, tile=tile)
             p = tcg.gemm_plan_for_caps(d, tcg.make_caps(lds_bytes=lds))
-            assert p.info().stages == want
+            bk = 64 if tile == 3 else 128
+            # 4 trips or fewer keep two slots
+            assert p.info().stages == (min(want, 2) if -(-K // bk) <= 4 else want)
             C = run(tcg, A, B, w, plan=p)[0]
             if ref is None:
                 ref = as_bits(C)
