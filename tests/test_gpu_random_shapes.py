@@ -1,0 +1,75 @@
+"""A seeded sweep of random problems through the C ABI against the oracle.
+
+Sizes from 1 to ~700 on every side (K from 0), ragged against every tile,
+operands fp16, bf16 or FP8, outputs fp32, fp16 or bf16, every activation,
+with and without a bias row, on the planner's choice or on an explicit tile
+(the persistent short-K tile where its limits allow).  Integer inputs must
+match exactly; Gaussian ones within the relative tolerance.
+"""
+import random
+
+import pytest
+import torch
+
+import gemm_workloads as gw
+from gemm_workloads import BF16, F16, F32, FP8
+from gpu_helpers import check_against_oracle, run
+
+pytestmark = pytest.mark.gpu
+
+SIXTEEN_BIT_TILES = [1, 2, 3, 4, 5, 6, 7]
+FP8_TILES = [8, 9, 10]
+
+
+def cases(n=60, seed=20261202):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        in_dtype = rng.choice([F16, BF16, FP8])
+        out_dtype = rng.choice([F32, F16, BF16])
+        M = rng.choice([1, 2, 31, 33, 64, 127, 129, 255, 300, 513, 700]) if rng.random() < 0.5 else rng.randint(1, 700)
+        if rng.random() < 0.3:  # a short-K, narrow-N problem
+            N = rng.choice([8, 56, 96, 136, 200, 288])
+            K = rng.choice([8, 16, 40, 64, 88, 96])
+        else:
+            N = rng.choice([1, 8, 96, 136, 256, 288, 300, 511]) if rng.random() < 0.5 else rng.randint(1, 700)
+            K = rng.choice([0, 1, 8, 16, 40, 64, 96, 128, 200, 520]) if rng.random() < 0.5 else rng.randint(1, 700)
+        epi = rng.choice([0, 1, 1, 2, 3, 4, 5])
+        bias = rng.random() < 0.3
+        dist = gw.INT4 if (rng.random() < 0.4 and epi in (0, 1) and not bias) else gw.NORMAL
+        short_k_ok = (in_dtype != FP8 and 0 < K <= 96 and K % 8 == 0 and 0 < N <= 288 and N % 8 == 0
+                      and epi in (0, 1) and not bias)
+        r = rng.random()
+        if short_k_ok and r < 0.6:
+            tile = 11
+        elif r < 0.45:
+            tile = 0
+        else:
+            tile = rng.choice(FP8_TILES if in_dtype == FP8 else SIXTEEN_BIT_TILES)
+        out.append((i, M, N, K, in_dtype, out_dtype, epi, bias, dist, tile))
+    return out
+
+
+@pytest.fixture(scope="module")
+def tcg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_core_gemm_amd as t
+    t.check_runtime()
+    return t
+
+
+@pytest.mark.parametrize("case", cases(), ids=lambda c: f"case{c[0]}")
+def test_random_problem_matches_the_oracle(tcg, case):
+    i, M, N, K, in_dtype, out_dtype, epi, bias, dist, tile = case
+    w = gw.custom(M, N, K, in_dtype, out_dtype, epi, dist, seed=1000 + i)
+    A, B = gw.make_inputs(w)
+    b = gw.draw_bias(N, gw.NORMAL, seed=2000 + i) if bias else None
+    split = 0 if tile == 11 else (3 if i % 7 == 0 and K > 256 else 0)
+    if K == 0:
+        A = torch.zeros(0, dtype=A.dtype)
+        B = torch.zeros(0, dtype=B.dtype)
+    C, _, p = run(tcg, A, B, w, tile=tile, bias=b, split_k=split)
+    if tile:
+        assert p.info().tile_id == tile
+    check_against_oracle(w, A, B, C, bias=b)
