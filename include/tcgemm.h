@@ -125,7 +125,7 @@ enum {
  * batch 1, 0 < K <= 96 and 0 < N <= 288 with K and N multiples of 8, no
  * bias, GEMM_EPI_NONE or GEMM_EPI_RELU, no split and none of the stage
  * flags (GEMM_E_ARG otherwise), and it gives the same bits as tile 5.  The
- * planner picks it for such problems with at least one block per CU.
+ * planner picks it for such problems with at least two blocks per CU.
  * `split_k` cuts K into that many ranges (1 .. 256; fewer if K has fewer
  * trips), or 0 for one range unless GEMM_FLAG_SPLIT_K lets the planner
  * choose. */

@@ -180,7 +180,10 @@ void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, in
   if (d.tile) {
     *tile = d.tile;
     if (!may_split) return;
-  } else if (shortk_fits(d) && d.M >= (int64_t)tcg::shortk::kBM * caps.num_cus) {
+  } else if (shortk_fits(d) && d.M >= 2 * (int64_t)tcg::shortk::kBM * caps.num_cus) {
+    // at least two blocks per workgroup, so that copies of later blocks
+    // overlap the products and stores of earlier ones (at one to two
+    // blocks, 40000 x 288 x 96, the 256 x 96 tile was level with it)
     *tile = 11;
     return;
   } else if (!fp8 && d.K <= 128 && d.N > 0 && d.N % 96 == 0) {

@@ -95,9 +95,9 @@ def test_stage_fallbacks_follow_lds_budget():
 
 
 def test_short_k_token_projection_takes_the_persistent_tile():
-    """Many rows, K <= 96 and N <= 288 (multiples of 8), at least one 128-row
-    block per CU: the persistent short-K kernel (tile 11), one workgroup per
-    CU (grid = CUs) over ceil(M / 128) blocks, three A slots."""
+    """Many rows, K <= 96 and N <= 288 (multiples of 8), at least two 128-row
+    blocks per CU: the persistent short-K kernel (tile 11), one workgroup
+    per CU (grid = CUs) over ceil(M / 128) blocks, three A slots."""
     i = plan(129600, 288, 96, F16, F16, EPI_NONE).info()
     assert (i.tile_id, i.bm, i.bn, i.bk, i.stages) == (11, 128, 288, 32, 3)
     assert (i.tiles_m, i.tiles_n, i.workgroups, i.trips) == (1013, 1, 256, 3)
@@ -105,6 +105,7 @@ def test_short_k_token_projection_takes_the_persistent_tile():
     assert i.mfma_per_run == 1013 * 4 * 9 * 6
     assert plan(129600, 288, 96, F16, F16, EPI_RELU).info().tile_id == 11
     assert plan(65536, 192, 64, BF16, F32, EPI_NONE).info().tile_id == 11
+    assert plan(65535, 192, 64, BF16, F32, EPI_NONE).info().tile_id != 11  # under two blocks per CU
     assert "persistent" in plan(129600, 288, 96, F16, F16, EPI_NONE).describe()
 
 

@@ -30,8 +30,8 @@ def raw(t):
     gw.custom(256, 256, 256, F16, F32, EPI_RELU, gw.INT4, seed=1, name="int_f16"),
     gw.custom(300, 200, 130, BF16, BF16, EPI_NONE, gw.NORMAL, seed=2, name="ragged_bf16"),
     gw.custom(130, 96, 256, FP8, F32, EPI_RELU, gw.NORMAL, seed=3, name="fp8"),
-    # enough rows for the persistent short-K tile (one 128-row block per CU or more)
-    gw.custom(40000, 288, 96, F16, F16, EPI_NONE, gw.NORMAL, seed=4, name="short_k_f16",
+    # enough rows for the persistent short-K tile (two 128-row blocks per CU or more)
+    gw.custom(70000, 288, 96, F16, F16, EPI_NONE, gw.NORMAL, seed=4, name="short_k_f16",
               dist_b=gw.Dist("normal", 0.0, 96 ** -0.5)),
 ], ids=lambda w: w.name)
 def test_c_client_matches_the_oracle(w, tmp_path):

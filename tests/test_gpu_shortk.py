@@ -111,3 +111,36 @@ def test_repeat_runs_identical(tcg):
     first = as_bits(C0)
     for _ in range(3):
         assert np.array_equal(as_bits(run(tcg, A, B, w, plan=p)[0]), first)
+
+
+def test_misaligned_output_takes_tile_5(tcg):
+    """C not 16-byte aligned (3 elements into its buffer): the run takes
+    tile 5's kernel with element stores; same bits, guard band untouched."""
+    w = gw.custom(3000, 200, 64, F16, F16, EPI_RELU, gw.NORMAL, seed=13)
+    A, B = gw.make_inputs(w)
+    C0, _, p = run(tcg, A, B, w, tile=11)
+    C1, buf, _ = run(tcg, A, B, w, plan=p, guard=3, sentinel=0x5A5A)
+    assert np.array_equal(as_bits(C0), as_bits(C1))
+    raw = as_bits(buf)
+    assert np.all(raw[:3] == np.int16(0x5A5A)) and np.all(raw[-3:] == np.int16(0x5A5A))
+
+
+def test_autotune_counts_the_persistent_tile(tcg):
+    """A short-K problem: the autotuner times tile 11 with the others and
+    the plan it keeps computes the product."""
+    tcg.gemm_tune_cache_clear()
+    w = gw.custom(40000, 288, 96, F16, F16, EPI_NONE, gw.NORMAL, seed=14,
+                  dist_b=gw.Dist("normal", 0.0, 96 ** -0.5))
+    A, B = gw.make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    C = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    desc = tcg.make_desc(w.M, w.N, w.K, F16, F16, EPI_NONE)
+    assert tcg.gemm_plan_for_caps(tcg.make_desc(w.M, w.N, w.K, F16, F16, EPI_NONE, tile=11),
+                                  tcg.gemm_device_caps_query(0)).info().tile_id == 11
+    p = tcg.gemm_autotune(desc, Ad, Bd, C)
+    note(f"autotune 40000x288x96 chose: {p.describe()}")
+    C.fill_(float("nan"))
+    tcg.gemm_run(p, Ad, Bd, C)
+    torch.cuda.synchronize()
+    check_against_oracle(w, A, B, C.cpu().reshape(1, w.M, w.N))
+    tcg.gemm_tune_cache_clear()
