@@ -846,15 +846,15 @@ void gemm_kernel(KArgs a) {
     // consecutive MFMAs share their first operand (measured about 2 % faster
     // than the transposed order on bf16 4096^3).  Each accumulator still
     // takes its k-steps in ascending order.
+    // The A blocks run up for even B blocks and down for odd ones, so that
+    // the two MFMAs on either side of a B change share their A operand too.
     auto mma_one = [&](const Frags& f, int m) __attribute__((always_inline)) {
-      const int i = m % FM, j = m / FM;
+      const int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
       acc[i][j] = mfma<BF16IN>(f.b[j], f.a[i], acc[i][j]);
     };
     auto mma = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][j] = mfma<BF16IN>(f.b[j], f.a[i], acc[i][j]);
+      for (int m = 0; m < FM * FN; ++m) mma_one(f, m);
     };
     auto wait_all_and_barrier = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
