@@ -118,8 +118,9 @@ enum {
 /* The problem.  M, N >= 0, K >= 0 (K == 0 gives C = epilogue(+0));
  * batch >= 1; with batch > 1, stride_a >= M*K, stride_b >= K*N and
  * stride_c >= M*N.  `tile` selects a tile configuration by id (1 ..
- * gemm_tile_count()), or 0 for the planner's choice; tiles 1-7 and 11 take
- * 16-bit operands and tiles 8-10 FP8 operands (another gives GEMM_E_ARG).
+ * gemm_tile_count()), or 0 for the planner's choice; tiles 1-7, 11 and 12
+ * take 16-bit operands and tiles 8-10 FP8 operands (another gives
+ * GEMM_E_ARG).
  * Tile 11 is the persistent short-K kernel (one workgroup per CU looping
  * over 128-row blocks, B held in LDS for the whole launch); it takes only
  * batch 1, 0 < K <= 96 and 0 < N <= 288 with K and N multiples of 8, no

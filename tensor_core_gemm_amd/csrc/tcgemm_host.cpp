@@ -116,6 +116,7 @@ TileCost tile_cost(int id) {
     case 2: case 9: return {2, 0.75, 0.90, false};
     case 3: case 10: return {2, 0.26, 0.42, false};  // three slots in flight
     case 7: return {2, 0.31, 0.54, false};
+    case 12: return {1, 0.65, 1.06, true};  // by id and in the autotuner only
     default: return {1, 1.0, 1.0, false};  // 4, 5: chosen by rule or by id
   }
 }
@@ -634,6 +635,7 @@ extern "C" int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void*
     case 8: e = (gen ? tcg::launch_t8_gen : tcg::launch_t8)(in.stages, vec16, bf16, a, s); break;
     case 9: e = (gen ? tcg::launch_t9_gen : tcg::launch_t9)(in.stages, vec16, bf16, a, s); break;
     case 10: e = (gen ? tcg::launch_t10_gen : tcg::launch_t10)(in.stages, vec16, bf16, a, s); break;
+    case 12: e = (gen ? tcg::launch_t12_gen : tcg::launch_t12)(in.stages, vec16, bf16, a, s); break;
     default: break;
   }
   if (e == hipSuccess && in.split_k > 1) {

@@ -31,6 +31,9 @@ hipError_t launch_t9_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipS
 hipError_t launch_t10(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t10_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 
+hipError_t launch_t12(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t12_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+
 // The persistent short-K kernel, tile 11 (tcgemm_shortk.hip): a.workgroups
 // workgroups loop over a.tiles_m blocks of 128 rows.
 hipError_t launch_t11(bool bf16, const KArgs& a, hipStream_t s);

@@ -205,7 +205,7 @@ def test_batch_strides(tcg):
     check_against_oracle(w, A, B, C)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 12])
 def test_every_tile_gives_the_exact_integer_result(tcg, tile):
     """Every tile configuration computes the same result (page "gizml:tile",
     tune requires all configurations to agree)."""
@@ -220,14 +220,14 @@ def test_every_tile_gives_the_exact_integer_result(tcg, tile):
 # the hand-interleaved trips only while chunk t + 2S exists, and then splits
 # each chunk's copies between two trips; the last trips issue whole chunks
 # and finish a split one.  K = BK * trips - 8 leaves a partial last chunk.
-TRIP_CASES = [(tile, trips, flags) for tile, flags in ((1, 0), (2, 0), (3, 0), (6, 0), (7, 0),
+TRIP_CASES = [(tile, trips, flags) for tile, flags in ((1, 0), (2, 0), (3, 0), (6, 0), (7, 0), (12, 0),
                                                        (3, "stages2"), (6, "stages2"), (7, "stages2"))
               for trips in range(1, 10)]
 
 
 @pytest.mark.parametrize("tile,trips,flags", TRIP_CASES)
 def test_trip_counts_across_the_copy_schedule(tcg, tile, trips, flags):
-    bk = 64 if tile in (1, 2, 3) else 32
+    bk = 64 if tile in (1, 2, 3, 12) else 32
     K = bk * trips - 8
     f = tcg.FLAG_FORCE_STAGES_2 if flags == "stages2" else 0
     w = gw.custom(300, 264, K, F16, F32, EPI_RELU, gw.INT4, seed=100 * tile + trips)
