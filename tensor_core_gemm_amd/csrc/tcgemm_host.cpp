@@ -117,6 +117,7 @@ TileCost tile_cost(int id) {
     case 3: case 10: return {2, 0.26, 0.42, false};  // three slots in flight
     case 7: return {2, 0.31, 0.54, false};
     case 12: return {1, 0.65, 1.06, true};  // by id and in the autotuner only
+    case 13: return {2, 0.38, 0.84, false};  // twice tile 3's work per trip
     default: return {1, 1.0, 1.0, false};  // 4, 5: chosen by rule or by id
   }
 }
@@ -171,9 +172,12 @@ constexpr int64_t kMinTripsPerSplit = 8;
 // products whose N is a multiple of 96 take the 256 x 96 tile (few trips,
 // many workgroups to stream A and C; measured faster than one 128 x 288 tile
 // per row block); the rest take the tile and split with the lowest
-// estimated time among 256 x 256, 128 x 128, 64 x 64 and the 128 x 128
-// ring of half-depth slots (which wins mid sizes such as 2048^3).  Tiles
-// 4-6 otherwise run only when asked for by id.  FP8 operands choose among
+// estimated time among 256 x 256, 128 x 128, 64 x 64, the 128 x 128
+// ring of half-depth slots (which wins mid sizes such as 2048^3) and the
+// 64 x 64 tile with 128-deep trips (half the trips, each with twice the
+// MFMAs: it wins grids of at most one workgroup per CU without ragged
+// tiles, 512^3 to 1024^3).
+// Tiles 4-6 and 12 otherwise run only when asked for by id.  FP8 operands choose among
 // their own tiles (8, 9, 10).
 void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, int* tile, int64_t* splits) {
   *splits = 1;
@@ -192,18 +196,25 @@ void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, in
     return;
   }
   double best_t = 1e300;
-  static const int kGeneral16[] = {1, 2, 3, 7}, kGeneral8[] = {8, 9, 10};
+  static const int kGeneral16[] = {1, 2, 3, 7, 13}, kGeneral8[] = {8, 9, 10};
   const int* ids = fp8 ? kGeneral8 : kGeneral16;
-  int n_ids = fp8 ? 3 : 4;
+  int n_ids = fp8 ? 3 : 5;
   if (d.tile) {
     ids = &d.tile;
     n_ids = 1;
   }
   for (int k = 0; k < n_ids; ++k) {
     const int id = ids[k];
-    const int64_t trips = cdiv(d.K, tile_desc(id).bk);
+    const auto& t = tile_desc(id);
+    const int64_t trips = cdiv(d.K, t.bk);
+    const int64_t grid = cdiv(d.M, t.bm) * cdiv(d.N, t.bn) * d.batch;
     for (int64_t sp = 1; sp <= kMaxSplits; sp *= 2) {
       if (sp > 1 && (!may_split || trips / sp < kMinTripsPerSplit)) break;
+      // The 128-deep 64 x 64 tile only where each CU runs at most one
+      // workgroup (1536^3, 2.25 per CU: 20.5 us against 17.9 for the
+      // 128 x 128 ring) and no tile is ragged (1000^3: 7.55 us against 7.45
+      // for the 64-deep tile; 1024^3: 6.65 against 7.17).
+      if (id == 13 && !d.tile && (grid * sp > caps.num_cus || d.M % t.bm || d.N % t.bn)) continue;
       const double est = estimate_us(d, caps, id, sp);
       if (est < best_t * 0.999) {
         best_t = est;
@@ -404,9 +415,20 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
   // With 4 trips or fewer a deeper ring only delays the first products
   // (measured on the 64 x 64 tile: 256^3, 4 trips, 3.7 us with two slots
   // and 4.0 us with three).
+  // A deeper ring that leaves room for fewer workgroups per CU than the
+  // tile is built for (the 64 x 64 x 128 tile: three 32 KiB slots) pays
+  // only while the grid runs in one round and K is long: measured on that
+  // tile, 1024^3 (8 trips) 6.7 us with two slots and 7.1 with three,
+  // 512 x 512 x 8192 39.2 and 26.9 us, 2048^3 (four workgroups per CU)
+  // 31.2 and 36.0 us.
   if (stages == 2 && t.max_stages > 2 && !(d.flags & GEMM_FLAG_FORCE_STAGES_2) && cdiv(d.K, t.bk) > 4) {
     const int64_t fit = (int64_t)caps->lds_bytes / (tiles[0] + tiles[1]);
-    stages = (int)std::min<int64_t>(t.max_stages, fit);
+    int deeper = (int)std::min<int64_t>(t.max_stages, fit);
+    const bool fewer_per_cu = (int64_t)t.min_waves * tcg::lds_bytes_for(t, deeper) > caps->lds_bytes;
+    const int64_t sp = std::max<int64_t>(want_splits, 1);
+    const int64_t grid = cdiv(d.M, t.bm) * cdiv(d.N, t.bn) * std::max<int64_t>(d.batch, 1) * sp;
+    if (fewer_per_cu && (cdiv(cdiv(d.K, t.bk), sp) <= 8 || grid > caps->num_cus)) deeper = 2;
+    stages = deeper;
   }
   if ((d.flags & GEMM_FLAG_FORCE_STAGES_1) && stages > 1) stages = 1;
 
@@ -636,6 +658,7 @@ extern "C" int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void*
     case 9: e = (gen ? tcg::launch_t9_gen : tcg::launch_t9)(in.stages, vec16, bf16, a, s); break;
     case 10: e = (gen ? tcg::launch_t10_gen : tcg::launch_t10)(in.stages, vec16, bf16, a, s); break;
     case 12: e = (gen ? tcg::launch_t12_gen : tcg::launch_t12)(in.stages, vec16, bf16, a, s); break;
+    case 13: e = (gen ? tcg::launch_t13_gen : tcg::launch_t13)(in.stages, vec16, bf16, a, s); break;
     default: break;
   }
   if (e == hipSuccess && in.split_k > 1) {

@@ -33,6 +33,8 @@ hipError_t launch_t10_gen(int stages, bool vec16, bool bf16, const KArgs& a, hip
 
 hipError_t launch_t12(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 hipError_t launch_t12_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t13(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
+hipError_t launch_t13_gen(int stages, bool vec16, bool bf16, const KArgs& a, hipStream_t s);
 
 // The persistent short-K kernel, tile 11 (tcgemm_shortk.hip): a.workgroups
 // workgroups loop over a.tiles_m blocks of 128 rows.

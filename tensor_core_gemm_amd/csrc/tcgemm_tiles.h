@@ -38,6 +38,7 @@ constexpr TileDesc kTiles[] = {
     {10, 64, 64, 128, 2, 2, 3, 2, 1},   // FP8, wave 32 x 32, up to 3 slots
     {11, 128, 288, 96, 4, 1, 3, 1, 2, 1},  // persistent short K: wave 32 x 288, B resident
     {12, 256, 128, 64, 2, 2, 2, 1, 2},  // wave 128 x 64: half the 256 x 256 tile's granularity
+    {13, 64, 64, 128, 2, 2, 3, 2, 2},   // wave 32 x 32, 128-deep trips, up to 3 slots: small latency-bound products
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 

@@ -152,6 +152,26 @@ def test_ragged_and_small_shapes_fill_the_chip():
     assert i.bm == 64
 
 
+def test_deep_trip_tile_takes_unragged_one_round_grids():
+    """The 64 x 64 tile with 128-deep trips: chosen where the grid gives each
+    CU at most one workgroup and no tile is ragged; its third slot (one
+    workgroup per CU) only past 8 trips on such a grid."""
+    for M, N, K in ((1024, 1024, 1024), (512, 512, 512), (768, 768, 768), (896, 1152, 1024), (256, 256, 256)):
+        i = plan(M, N, K).info()
+        assert (i.tile_id, i.bk, i.stages) == (13, 128, 2), (M, N, K)
+    assert plan(1000, 1000, 1000).info().tile_id == 3     # ragged edge tiles
+    assert plan(1536, 1536, 1536).info().tile_id == 7     # 2.25 workgroups per CU
+    assert plan(2048, 2048, 2048).info().tile_id == 7
+    i = plan(512, 512, 8192).info()
+    assert (i.tile_id, i.stages) == (13, 3)
+    assert plan(1024, 1024, 1152).info().stages == 3     # 9 trips, one round
+    assert plan(2048, 2048, 2048, tile=13).info().stages == 2   # four per CU
+    assert plan(1024, 1024, 1024, tile=13).info().stages == 2   # 8 trips
+    assert plan(64, 64, 8192, tile=13, split_k=8).info().stages == 2  # 8 trips per range
+    assert plan(64, 64, 8192, tile=13, split_k=4).info().stages == 3
+    assert plan(512, 512, 8192, tile=13, flags=tcg.FLAG_FORCE_STAGES_2).info().stages == 2
+
+
 def test_vec16_needs_aligned_rows():
     assert plan(100, 64, 24).info().vec16 == 1
     assert plan(100, 64, 13).info().vec16 == 0

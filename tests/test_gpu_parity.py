@@ -176,6 +176,28 @@ def test_small_tile_rings_give_the_same_bits(tcg, tile, in_dtype):
             assert np.array_equal(as_bits(C), ref), (M, N, K, want)
 
 
+@pytest.mark.parametrize("in_dtype", [F16, BF16])
+def test_deep_trip_tile_rings_give_the_same_bits(tcg, in_dtype):
+    """The 64 x 64 tile with 128-deep trips takes three slots only for more
+    than 8 trips on a grid of at most one workgroup per CU; every ring depth,
+    one stage and no staging give the same bits (ragged edges, K tails)."""
+    for M, N, K, deep in ((1000, 1000, 1000, False), (130, 70, 1400, True), (64, 64, 1032, True),
+                          (300, 200, 4000, True), (2048, 1024, 1152, False)):
+        w = gw.custom(M, N, K, in_dtype, F32, EPI_RELU, gw.NORMAL, seed=K + M)
+        A, B = gw.make_inputs(w)
+        ref = None
+        for flags, want in ((0, 3 if deep else 2), (tcg.FLAG_FORCE_STAGES_2, 2), (tcg.FLAG_FORCE_STAGES_1, 1),
+                            (tcg.FLAG_UNSTAGED, 0)):
+            d = tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, flags, tile=13)
+            p = tcg.gemm_plan_for_caps(d, tcg.make_caps())
+            assert p.info().stages == want, (M, N, K, flags)
+            C = run(tcg, A, B, w, plan=p)[0]
+            if ref is None:
+                ref = as_bits(C)
+                check_against_oracle(w, A, B, C)
+            assert np.array_equal(as_bits(C), ref), (M, N, K, want)
+
+
 def test_repeat_runs_identical(tcg):
     w = W["ragged_fp16_1000"]
     A, B = gw.make_inputs(w)
@@ -205,7 +227,7 @@ def test_batch_strides(tcg):
     check_against_oracle(w, A, B, C)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 12])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 12, 13])
 def test_every_tile_gives_the_exact_integer_result(tcg, tile):
     """Every tile configuration computes the same result (page "gizml:tile",
     tune requires all configurations to agree)."""
@@ -220,14 +242,15 @@ def test_every_tile_gives_the_exact_integer_result(tcg, tile):
 # the hand-interleaved trips only while chunk t + 2S exists, and then splits
 # each chunk's copies between two trips; the last trips issue whole chunks
 # and finish a split one.  K = BK * trips - 8 leaves a partial last chunk.
-TRIP_CASES = [(tile, trips, flags) for tile, flags in ((1, 0), (2, 0), (3, 0), (6, 0), (7, 0), (12, 0),
-                                                       (3, "stages2"), (6, "stages2"), (7, "stages2"))
+TRIP_CASES = [(tile, trips, flags) for tile, flags in ((1, 0), (2, 0), (3, 0), (6, 0), (7, 0), (12, 0), (13, 0),
+                                                       (3, "stages2"), (6, "stages2"), (7, "stages2"),
+                                                       (13, "stages2"))
               for trips in range(1, 10)]
 
 
 @pytest.mark.parametrize("tile,trips,flags", TRIP_CASES)
 def test_trip_counts_across_the_copy_schedule(tcg, tile, trips, flags):
-    bk = 64 if tile in (1, 2, 3, 12) else 32
+    bk = {13: 128, 1: 64, 2: 64, 3: 64, 12: 64}.get(tile, 32)
     K = bk * trips - 8
     f = tcg.FLAG_FORCE_STAGES_2 if flags == "stages2" else 0
     w = gw.custom(300, 264, K, F16, F32, EPI_RELU, gw.INT4, seed=100 * tile + trips)

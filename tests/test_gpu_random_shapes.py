@@ -17,7 +17,7 @@ from gpu_helpers import check_against_oracle, run
 
 pytestmark = pytest.mark.gpu
 
-SIXTEEN_BIT_TILES = [1, 2, 3, 4, 5, 6, 7, 12]
+SIXTEEN_BIT_TILES = [1, 2, 3, 4, 5, 6, 7, 12, 13]
 FP8_TILES = [8, 9, 10]
 
 
