@@ -74,7 +74,8 @@ SWEEP = [(512, 512, 512), (1024, 1024, 1024), (2048, 2048, 2048), (2304, 2304, 2
          (3000, 3000, 3000), (4096, 4096, 4096), (6144, 6144, 6144), (8192, 8192, 8192),
          (1024, 4096, 4096), (4096, 1024, 4096), (4096, 4096, 1024), (256, 4096, 4096),
          (4096, 256, 4096), (128, 8192, 8192), (512, 8192, 8192), (8192, 1024, 1024),
-         (16384, 16384, 1024), (2048, 2048, 8192), (512, 512, 16384), (1024, 1024, 32768)]
+         (16384, 16384, 1024), (2048, 2048, 8192), (512, 512, 16384), (1024, 1024, 32768),
+         (4608, 4608, 4608), (7168, 7168, 7168)]
 
 
 def planner_sweep():
@@ -116,6 +117,8 @@ def planner_sweep():
             us = timed(lambda: tcg.gemm_run_ex(p, A, B, C, workspace=w))
             row[name] = {"us": round(us, 2), "tflops": round(tflop / us * 1e6, 1),
                          "tile": i.tile_id, "split": i.split_k}
+            if i.tail_rows:
+                row[name]["tail"] = [i.tail_rows, i.tail_split]
         us = timed(lambda: torch.matmul(A, B, out=C))
         row["torch_matmul"] = {"us": round(us, 2), "tflops": round(tflop / us * 1e6, 1)}
         print(json.dumps(row), flush=True)

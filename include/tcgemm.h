@@ -21,6 +21,15 @@
  * rounding only.  Every path of one plan (staged, one stage, unstaged)
  * splits the same way and returns the same bits.
  *
+ * With GEMM_FLAG_SPLIT_K the planner may also split K for the bottom rows
+ * only (gemm_plan_info.tail_rows > 0): where the output tiles fill some
+ * whole rounds of the device's CUs and leave a small last round, the rows
+ * of the whole rounds run unsplit and the last tail_rows rows run as a
+ * second launch (same stream) with K cut into tail_split ranges, so that
+ * the last round occupies more CUs.  Rows above the tail return the
+ * unsplit plan's bits; tail rows return the bits of a plan split into
+ * tail_split ranges.
+ *
  * Elements outside the matrices read as 0 (In.at) and elements outside C are
  * never written (Out.put leaves the rest of C as it was).  The staged kernel
  * and the unstaged kernel of the same plan perform the same MFMA sequence on
@@ -84,8 +93,9 @@ enum {
  *     bias[j] added to column j of every row of every batch item (passed
  *     to gemm_run_ex).
  *   GEMM_FLAG_SPLIT_K: with split_k == 0, let the planner split K where
- *     that is estimated faster (few output tiles, long K); such a plan
- *     needs a workspace (gemm_plan_info.workspace_bytes).
+ *     that is estimated faster (few output tiles, long K), or split it for
+ *     the bottom rows only (a small last round of tiles, batch 1); such a
+ *     plan needs a workspace (gemm_plan_info.workspace_bytes).
  *   GEMM_FLAG_TUNED: with tile == 0 and split_k == 0, take the choice an
  *     earlier gemm_autotune measured for this problem on this device, if
  *     any (else the planner's). */
@@ -172,6 +182,13 @@ typedef struct gemm_plan_info {
   int32_t split_k;          /* K ranges (1: no split)                        */
   int64_t trips_per_split;  /* trips of each K range (the last may have fewer) */
   int64_t workspace_bytes;  /* device workspace a run needs (0 without split) */
+  int64_t tail_rows;        /* > 0: the last tail_rows rows of C run as a second
+                               launch with K split into tail_split ranges (the
+                               other fields describe the rows above, except
+                               workgroups, mfma_per_run and workspace_bytes,
+                               which cover both launches); 0: none          */
+  int32_t tail_split;       /* K ranges of the tail rows (0 without a tail)  */
+  int32_t reserved0;
 } gemm_plan_info;
 
 typedef struct gemm_plan_s* gemm_plan_t;

@@ -53,7 +53,8 @@ class gemm_plan_info(ctypes.Structure):
                 ("mfma_per_run", ctypes.c_int64), ("mfma_m", ctypes.c_int32),
                 ("mfma_n", ctypes.c_int32), ("mfma_k", ctypes.c_int32),
                 ("split_k", ctypes.c_int32), ("trips_per_split", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_int64), ("tail_rows", ctypes.c_int64),
+                ("tail_split", ctypes.c_int32), ("reserved0", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -327,6 +327,31 @@ def test_planner_splits_only_when_allowed_and_useful():
     assert plan(256, 256, 256, flags=tcg.FLAG_SPLIT_K).info().split_k == 1
 
 
+def test_split_tail_for_a_small_last_round():
+    """With GEMM_FLAG_SPLIT_K, a problem whose tiles fill whole rounds of the
+    CUs and leave a small last round runs the rows of the whole rounds
+    unsplit and splits K for the rest; not where the last round is large,
+    K is short, or the tile, the split or the batch is fixed."""
+    S = tcg.FLAG_SPLIT_K
+    i = plan(6144, 6144, 6144, flags=S).info()
+    assert (i.tile_id, i.split_k, i.tail_rows, i.tail_split) == (1, 1, 768, 3)
+    assert i.tiles_m == 21 and i.workgroups == 21 * 24 + 3 * 24 * 3
+    assert i.workspace_bytes == 3 * 768 * 6144 * 4
+    assert "last 768 rows a second launch, split K 3 x 32 trips" in plan(6144, 6144, 6144, flags=S).describe()
+    i = plan(4608, 4608, 4608, flags=S).info()
+    assert (i.tail_rows, i.tail_split) == (1024, 3)
+    i = plan(7168, 7168, 7168, flags=S).info()
+    assert (i.tail_rows, i.tail_split) == (256, 8)
+    for M, N, K in ((5120, 5120, 5120), (6144, 6144, 2048), (4096, 4096, 4096), (8192, 8192, 8192)):
+        assert plan(M, N, K, flags=S).info().tail_rows == 0, (M, N, K)
+    assert plan(6144, 6144, 6144).info().tail_rows == 0                    # no flag
+    assert plan(6144, 6144, 6144, flags=S, tile=1).info().tail_rows == 0   # tile by id
+    assert plan(6144, 6144, 6144, flags=S, split_k=1).info().tail_rows == 0
+    i = plan(6144, 6144, 6144, flags=S, batch=2, sa=6144 * 6144, sb=6144 * 6144, sc=6144 * 6144).info()
+    assert i.tail_rows == 0
+    assert plan(4096, 4096, 4096, flags=S).info().tail_split == 0
+
+
 def test_epilogue_is_named_in_the_description():
     for epi, name in ((0, "none"), (1, "relu"), (2, "gelu"), (3, "gelu_erf"), (4, "sigmoid"), (5, "tanh")):
         assert f"epilogue {name}" in plan(64, 64, 64, epi=epi).describe()
