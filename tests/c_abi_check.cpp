@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "tcgemm.h"
@@ -35,10 +36,12 @@ static bool read_file(const char* path, std::vector<unsigned char>& out, size_t 
   } while (0)
 
 int main(int argc, char** argv) {
-  if (argc != 10) {
-    std::fprintf(stderr, "usage: %s M N K in_dtype out_dtype epilogue a.bin b.bin c.bin\n", argv[0]);
+  if (argc != 10 && argc != 11) {
+    std::fprintf(stderr, "usage: %s M N K in_dtype out_dtype epilogue a.bin b.bin c.bin [split]\n", argv[0]);
     return 2;
   }
+  // "split": let the planner split K (GEMM_FLAG_SPLIT_K) and run with a workspace
+  const bool split = argc == 11 && std::strcmp(argv[10], "split") == 0;
   const int64_t M = std::atoll(argv[1]), N = std::atoll(argv[2]), K = std::atoll(argv[3]);
   const int in_dtype = std::atoi(argv[4]), out_dtype = std::atoi(argv[5]), epi = std::atoi(argv[6]);
   const size_t isz = in_dtype == GEMM_FP8 ? 1 : 2, osz = out_dtype == GEMM_F32 ? 4 : 2;
@@ -70,6 +73,7 @@ int main(int argc, char** argv) {
   d.out_dtype = out_dtype;
   d.epilogue = epi;
   d.batch = 1;
+  if (split) d.flags = GEMM_FLAG_SPLIT_K;
   gemm_plan_t plan = nullptr;
   int rc = gemm_plan(&d, &plan);
   if (rc != GEMM_OK) {
@@ -77,12 +81,21 @@ int main(int argc, char** argv) {
     return 5;
   }
   std::printf("plan: %s\n", gemm_plan_describe(plan));
+  gemm_plan_info info;
+  if (gemm_plan_get_info(plan, &info) != GEMM_OK) return 5;
+  std::printf("info: split_k %d tail_rows %lld tail_split %d workspace %lld\n", info.split_k,
+              (long long)info.tail_rows, info.tail_split, (long long)info.workspace_bytes);
+  void* dW = nullptr;
+  if (info.workspace_bytes > 0) CHECK_HIP(hipMalloc(&dW, (size_t)info.workspace_bytes));
+  gemm_run_args args = {};
+  args.workspace = dW;
+  args.workspace_bytes = info.workspace_bytes;
   // C overlapping A is refused before anything runs.
-  if (gemm_run(plan, dA, dB, dA, nullptr) != GEMM_E_ALIAS) return 4;
+  if (gemm_run_ex(plan, dA, dB, dA, &args, nullptr) != GEMM_E_ALIAS) return 4;
 
   hipStream_t s;
   CHECK_HIP(hipStreamCreate(&s));
-  rc = gemm_run(plan, dA, dB, dC, s);
+  rc = gemm_run_ex(plan, dA, dB, dC, &args, s);
   if (rc != GEMM_OK) {
     std::fprintf(stderr, "gemm_run: %s\n", gemm_strerror(rc));
     return 5;
@@ -98,6 +111,7 @@ int main(int argc, char** argv) {
   CHECK_HIP(hipFree(dA));
   CHECK_HIP(hipFree(dB));
   CHECK_HIP(hipFree(dC));
+  if (dW) CHECK_HIP(hipFree(dW));
   std::printf("ok\n");
   return 0;
 }
