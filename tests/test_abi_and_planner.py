@@ -350,6 +350,8 @@ def test_split_tail_for_a_small_last_round():
     i = plan(6144, 6144, 6144, flags=S, batch=2, sa=6144 * 6144, sb=6144 * 6144, sc=6144 * 6144).info()
     assert i.tail_rows == 0
     assert plan(4096, 4096, 4096, flags=S).info().tail_split == 0
+    i = plan(4608, 4608, 8192, in_dtype=tcg.FP8, flags=S).info()   # FP8: the 256 x 256 x 128 tile
+    assert (i.tile_id, i.tail_rows, i.tail_split) == (8, 1024, 3)
 
 
 def test_epilogue_is_named_in_the_description():

@@ -124,3 +124,16 @@ def test_captured_runs_replay_the_eager_result(tcg):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(as_bits(C.cpu()), eager), f"replay {r}"
+
+
+def test_fp8_tail_exact_on_integers(tcg):
+    # FP8 operands on the 256 x 256 x 128 tile: 4608 x 4608 x 8192 runs its
+    # last 1024 rows in 3 K ranges; sums of at most 16 * 8192 are exact
+    w = gw.custom(4608, 4608, 8192, gw.FP8, F32, EPI_RELU, gw.INT4, seed=75)
+    A, B = gw.make_inputs(w)
+    C, _, p = run(tcg, A, B, w, flags=tcg.FLAG_SPLIT_K)
+    i = p.info()
+    assert (i.tile_id, i.tail_rows, i.tail_split) == (8, 1024, 3)
+    check_sampled(w, A, B, C, count=8192)
+    C1, _, _ = run(tcg, A, B, w, tile=8, split_k=1)
+    assert np.array_equal(as_bits(C), as_bits(C1))
