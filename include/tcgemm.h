@@ -128,7 +128,7 @@ enum {
 /* The problem.  M, N >= 0, K >= 0 (K == 0 gives C = epilogue(+0));
  * batch >= 1; with batch > 1, stride_a >= M*K, stride_b >= K*N and
  * stride_c >= M*N.  `tile` selects a tile configuration by id (1 ..
- * gemm_tile_count()), or 0 for the planner's choice; tiles 1-7, 11 and 12
+ * gemm_tile_count()), or 0 for the planner's choice; tiles 1-7 and 11-13
  * take 16-bit operands and tiles 8-10 FP8 operands (another gives
  * GEMM_E_ARG).
  * Tile 11 is the persistent short-K kernel (one workgroup per CU looping
