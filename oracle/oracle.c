@@ -29,6 +29,9 @@
  * about 1e-16 |v| on results that small):
  *     relu(v)    = v > 0 ? v : +0
  *     gelu(v)    = v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3)))   (tanh form)
+ *                  (the page names the tanh form but prints no constants;
+ *                  these are the published approximation of x Phi(x) of
+ *                  Hendrycks and Gimpel, "Gaussian Error Linear Units", 2016)
  *     geluErf(v) = v/2 * (1 + erf(v / sqrt(2)))                          (erf form)
  *     sigmoid(v) = 1 / (1 + e^-v)
  *     tanh(v)    = tanh(v)

@@ -142,3 +142,54 @@ def test_bias_is_shared_by_batch_items_and_sampled_agrees():
     out, Ys = oracle.gemm_sampled(A, B, M, N, K, BF16, F32, EPI_TANH, bi.ravel(), ii.ravel(),
                                   jj.ravel(), batch=batch, bias=bias)
     assert np.array_equal(Ys, Y1.ravel())
+
+
+# Wide grid for the GELU tanh form: every fp16-exact value in [-8, 8) at
+# steps of 1/64, plus a log-spaced sweep of magnitudes out to 30 (fp32
+# values, exact in fp16 after encoding) where x^3 dominates the argument.
+def _wide_gelu_grid():
+    mags = np.geomspace(1e-3, 30.0, 2001)
+    wide = np.concatenate([mags, -mags]).astype(np.float32)
+    wide = oracle.decode(F16, oracle.encode(F16, wide))  # exact as fp16 operands
+    return np.unique(np.concatenate([X, wide]))
+
+
+def test_gelu_tanh_form_matches_torch_in_double():
+    # An implementation other than the oracle's: torch's GELU with
+    # approximate="tanh", evaluated on float64 tensors, then rounded once to
+    # fp32 as the oracle does.  The form x(1 + tanh(sqrt(2/pi)(x + c x^3)))/2
+    # is the published tanh approximation of x Phi(x) (Hendrycks and Gimpel,
+    # "Gaussian Error Linear Units", 2016), c = 0.044715.  A change of c in
+    # its fifth digit, or of sqrt(2/pi) by 1e-3, moves many grid points by
+    # tens of ulps; the bound below admits only double's own rounding.
+    import torch
+    xs = _wide_gelu_grid()
+    got = act_of(xs, EPI_GELU)
+    want = torch.nn.functional.gelu(torch.from_numpy(xs.astype(np.float64)),
+                                    approximate="tanh").numpy()
+    # Below -5, 1 + tanh cancels in double (both sides evaluate the same
+    # form), leaving an absolute error of about 1e-16 |x| on top of the one
+    # fp32 rounding: there the bound is one fp32 ulp of the result plus that.
+    tail = xs < -5
+    assert ulps(got[~tail], want[~tail].astype(np.float32)).max() <= 1
+    w32 = want[tail].astype(np.float32)
+    bound = np.spacing(np.abs(w32)).astype(np.float64) + 4e-16 * np.abs(xs[tail])
+    assert np.all(np.abs(got[tail].astype(np.float64) - want[tail]) <= bound)
+
+
+def test_gelu_tanh_form_constants_are_observable():
+    # Guard the pin above: perturbing either constant in a double-precision
+    # twin of the form moves the result by more than the 1-ulp bound on this
+    # grid, so the pin could not pass with a wrong constant.
+    xs = _wide_gelu_grid().astype(np.float64)
+    xs = xs[xs > -5]
+
+    def form(c, s):
+        return (0.5 * xs * (1.0 + np.tanh(s * (xs + c * xs ** 3)))).astype(np.float32)
+
+    import torch
+    ref = torch.nn.functional.gelu(torch.from_numpy(xs), approximate="tanh").numpy().astype(np.float32)
+    s0 = np.sqrt(2.0 / np.pi)
+    assert ulps(form(0.044715, s0), ref).max() <= 1
+    assert ulps(form(0.0447, s0), ref).max() > 1
+    assert ulps(form(0.044715, s0 * 1.001), ref).max() > 1

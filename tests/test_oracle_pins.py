@@ -356,3 +356,25 @@ def test_workload_integer_config_is_exact_by_bound():
     exact = A.double().numpy().astype(np.int64) @ B.double().numpy().astype(np.int64)
     assert np.array_equal(C, np.maximum(exact, 0).astype(np.float32))
     assert math.isclose(w.sigma_out(), math.sqrt(256) * (80 / 12), rel_tol=1e-12)
+
+
+@pytest.mark.parametrize("in_dtype", [F16, BF16])
+def test_f64_twin_sums_exactly_on_integers(in_dtype):
+    # The fp64 twin's two outputs against int64 arithmetic: with integer
+    # operands every partial sum is an integer far below 2^53, so Y64 must
+    # equal A.B and S64 must equal |A|.|B| exactly (a doubled, dropped or
+    # signed term in either fails).  Batch items with padding between them
+    # check the strides.
+    rng = np.random.default_rng(21)
+    M, N, K, batch = 9, 13, 300, 2
+    sa, sb = M * K + 5, K * N + 3
+    Aall = rng.integers(-40, 41, batch * sa)
+    Ball = rng.integers(-40, 41, batch * sb)
+    Y64, S64 = oracle.gemm_f64(bits_of(in_dtype, Aall.astype(np.float32)),
+                               bits_of(in_dtype, Ball.astype(np.float32)), M, N, K, in_dtype,
+                               batch=batch, stride_a=sa, stride_b=sb)
+    for b in range(batch):
+        a = Aall[b * sa:b * sa + M * K].reshape(M, K).astype(np.int64)
+        bb = Ball[b * sb:b * sb + K * N].reshape(K, N).astype(np.int64)
+        assert np.array_equal(Y64[b], (a @ bb).astype(np.float64))
+        assert np.array_equal(S64[b], (np.abs(a) @ np.abs(bb)).astype(np.float64))
