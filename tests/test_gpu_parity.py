@@ -35,15 +35,24 @@ SMALL = ["int_fp16_256", "ragged_fp16_1000"]
 BIG = ["bf16_4096_relu", "swin_proj_fp16", "deepk_bf16_2048x16384"]
 
 # The large workloads' dtype, epilogue and input recipe at sizes the oracle
-# computes in full within seconds, each spanning several tiles and a ragged tail.
+# computes in full within seconds, each spanning several tiles and a ragged
+# tail in M and N, on the full-size plan's tile, split and copy path: K and
+# N are multiples of 8 so the 16-byte copies run, and the tile and split are
+# those the planner gives the full-size workload with split K allowed (the
+# benchmark's plan).
 SCALED = {
-    "bf16_4096_relu": gw.custom(600, 520, 700, BF16, BF16, EPI_RELU, gw.NORMAL, seed=21,
-                                name="bf16_relu_600x520x700"),
+    "bf16_4096_relu": gw.custom(600, 520, 704, BF16, BF16, EPI_RELU, gw.NORMAL, seed=21,
+                                name="bf16_relu_600x520x704"),
     "swin_proj_fp16": gw.custom(3000, 288, 96, F16, F16, EPI_NONE, gw.NORMAL, seed=31,
                                 dist_b=gw.Dist("normal", 0.0, 96 ** -0.5), name="swin_3000"),
-    "deepk_bf16_2048x16384": gw.custom(300, 260, 4000, BF16, BF16, EPI_NONE, gw.NORMAL, seed=51,
-                                       name="deepk_300x260x4000"),
+    "deepk_bf16_2048x16384": gw.custom(300, 264, 4096, BF16, BF16, EPI_NONE, gw.NORMAL, seed=51,
+                                       name="deepk_300x264x4096"),
 }
+
+
+def full_size_plan(tcg, w):
+    return tcg.gemm_plan(tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
+                                       tcg.FLAG_SPLIT_K)).info()
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -56,9 +65,14 @@ def test_small_workloads_full(tcg, name):
 
 @pytest.mark.parametrize("name", BIG)
 def test_scaled_workloads_full(tcg, name):
+    full = full_size_plan(tcg, W[name])
     w = SCALED[name]
     A, B = gw.make_inputs(w)
-    C, _, _ = run(tcg, A, B, w)
+    split = full.split_k if full.split_k > 1 else 0
+    C, _, p = run(tcg, A, B, w, tile=full.tile_id, split_k=split)
+    i = p.info()
+    assert (i.tile_id, i.stages, i.vec16, i.split_k) == (full.tile_id, full.stages, full.vec16,
+                                                         full.split_k)
     check_against_oracle(w, A, B, C)
 
 
