@@ -3,9 +3,10 @@
 
 A step is one gemm_run of the workload over inputs already resident in HBM
 (the planner's plan, split K allowed: a split plan's step is the GEMM and
-its reduction).  Launched back to back, the first ~100 GEMMs see the clock
-dip and recover as power management reacts; the default 200 warm-up steps
-put the timed steps in the settled state a sustained caller sees.
+its reduction).  Launched back to back, the first few hundred GEMMs see the
+clock boost, dip and recover as power management reacts; the default 400
+warm-up steps put the timed steps in the settled state a sustained caller
+sees.
 Default workload: bf16 M = N = K = 4096, A, B ~ N(0, 1), relu, bf16 out
 (the headline GEMM).  W untimed warm-up steps, then K timed steps between
 two device synchronisations; the average launch duration of the kernel is
@@ -15,9 +16,18 @@ roofline: the kernel is bound by the MFMA units; achieved = 2*M*N*K flops
 per launch / average launch duration, against MI355X's published dense
 fp16/bf16 MFMA peak (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096 flop/CU/clk).
 
+Also reported: the shader clock measured over the timed region (a probe
+kernel reads the shader-clock and constant-rate counters on every XCD just
+before and just after it), and the median, minimum and maximum launch
+duration from a separate pass with an event after every launch.
+
 cpu_baseline: the CPU oracle (plain C, fp32, OpenMP) timed on this host's
 cores on a bounded sample of the same workload: the first r rows of C
-(r x N x K multiply-adds), r chosen so the oracle works about 10-20 s.
+(r x N x K multiply-adds), r chosen so the oracle works about 12 s; then on
+one thread (about 6 s); with the CPU model.
+
+--mfma-ceiling: the register-only MFMA loop instead of the GEMM (the MFMA
+units' sustained rate on N(0, 1) bf16 operands and the clock they run at).
 """
 from __future__ import annotations
 
@@ -42,9 +52,10 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed launches first: back to back, the clock dips for about the first "
-                         "100 launches and then settles (power management), so 200 reach the steady state")
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="untimed launches first: back to back, the shader clock boosts, dips and "
+                         "recovers under power management for about the first 300-400 launches of "
+                         "~0.1 ms before it settles")
     ap.add_argument("--workload", default="bf16_4096_relu")
     ap.add_argument("--tile", type=int, default=0, help="force a tile configuration id")
     ap.add_argument("--flags", type=int, default=0, help="plan flags (1: one stage, 2: unstaged)")
@@ -63,6 +74,18 @@ def parse():
                          "the same way, with the activation as a separate op; reported as context")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--launch-samples", type=int, default=100,
+                    help="after the timed region, this many more launches each followed by an "
+                         "event, for the median and minimum launch duration")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the GEMM: the register-only MFMA loop (bf16 32x32x16, operands "
+                         "drawn from N(0, 1)) on every CU, timed the same way (the throughput the "
+                         "MFMA units sustain on this data with no memory traffic)")
+    ap.add_argument("--ceiling-dtype", choices=["bf16", "fp8"], default="bf16",
+                    help="operand type of the --mfma-ceiling loop (fp8: v_mfma_f32_32x32x64_f8f6f4 "
+                         "with E4M3 operands)")
+    ap.add_argument("--ceiling-iters", type=int, default=0,
+                    help="rounds of 64 MFMAs per wave in one --mfma-ceiling launch")
     ap.add_argument("--planner-sweep", action="store_true",
                     help="instead of the bench line: for a sweep of bf16 relu shapes, time the "
                          "planner's choice, the autotuner's and torch.matmul (one JSON line each)")
@@ -145,6 +168,9 @@ def main():
     if args.planner_sweep:
         planner_sweep()
         return
+    if args.mfma_ceiling:
+        mfma_ceiling(args)
+        return
     w = gw.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -188,6 +214,10 @@ def main():
         else:
             tcg.gemm_run_ex(plan, A, B, C, workspace=ws, stream=stream)
 
+    # made before the warm-up: allocating it between the warm-up and the
+    # timed region idled the GPU for milliseconds, which restarts the power
+    # manager's boost-dip-settle cycle (measured: ~15 % slower timed launches)
+    clock = make_clock_probe()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -200,14 +230,18 @@ def main():
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    clock.mark(0, stream)
     e_start.record(stream)
     for i in range(K):
         step(i)
     e_end.record(stream)
+    clock.mark(1, stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     avg_launch_ms = e_start.elapsed_time(e_end) / K
     ms_per_step = (t1 - t0) * 1e3 / K
+    clock_measured = clock.result()
+    per_launch = per_launch_times(step, args.launch_samples, stream)
 
     flops = w.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -261,7 +295,9 @@ def main():
             "in": gw.DTYPE_NAME[w.in_dtype], "out": gw.DTYPE_NAME[w.out_dtype],
             "epilogue": "relu" if w.epilogue else "none", "accumulate": "f32",
             "plan": plan.describe(), "pct_of_peak": round(100 * value / peak_mfma, 2),
-            "device": caps.arch.decode(), "cus": caps.num_cus, "clock_mhz": caps.clock_khz // 1000,
+            "device": caps.arch.decode(), "cus": caps.num_cus,
+            "peak_clock_mhz": caps.clock_khz // 1000,
+            "clock_mhz_measured": clock_measured,
             "input_sets": args.rotate,
             "sample_max_rel_err": sample_err,
         },
@@ -273,6 +309,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_avg_ms": round(avg_launch_ms, 5),
+            "launch_ms": per_launch,
             "flops_per_launch": flops,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes,
         },
@@ -282,6 +319,91 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, A_cpu, B_cpu, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def make_clock_probe():
+    from tensor_core_gemm_amd.probe import ClockProbe
+    return ClockProbe()
+
+
+def per_launch_times(step, n, stream):
+    """n more launches, each followed by an event on the launch stream:
+    the median, minimum and maximum of the per-launch durations (a pass of
+    its own, after the timed region, so the events do not touch the
+    region's average)."""
+    import numpy as np
+    import torch
+    if n <= 0:
+        return None
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    return {"n": n, "median": round(float(np.median(d)), 5), "min": round(float(d.min()), 5),
+            "max": round(float(d.max()), 5), "mean": round(float(d.mean()), 5)}
+
+
+def mfma_ceiling(args):
+    """The register-only MFMA loop on every CU: the MFMA units' sustained
+    rate on N(0, 1) bf16 operands with no memory traffic, LDS or barriers,
+    and the shader clock it runs at."""
+    import numpy as np
+    import torch
+
+    import gemm_workloads as gw
+    import tensor_core_gemm_amd as tcg
+    from tensor_core_gemm_amd import probe
+
+    caps = tcg.gemm_device_caps_query(0)
+    wg = caps.num_cus
+    gen = torch.Generator().manual_seed(7)
+    fp8 = args.ceiling_dtype == "fp8"
+    if fp8:
+        ops = gw.draw((16 * 64 * 32,), gw.NORMAL, gw.FP8, gen).view(torch.uint8).cuda()
+        kind, iters = probe.MFMA_32x32x64_FP8, args.ceiling_iters or 35
+    else:
+        ops = gw.draw((16 * 64 * 8,), gw.NORMAL, gw.BF16, gen).view(torch.int16).cuda()
+        kind, iters = probe.MFMA_32x32x16_BF16, args.ceiling_iters or 70
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    ticks = torch.zeros(wg, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i=0):
+        return probe.mfma_rate(kind, wg, iters, ops, sink, ticks, stream)
+
+    flops = step()
+    clock = probe.ClockProbe()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clock.mark(0, stream)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    clock.mark(1, stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per_launch = per_launch_times(step, args.launch_samples, stream)
+    cyc = ticks.cpu().numpy().astype(np.float64)
+    mfmas_per_wave = iters * 64
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[gw.FP8 if fp8 else gw.BF16]
+    name = ("v_mfma_f32_32x32x64_f8f6f4, E4M3" if fp8 else "v_mfma_f32_32x32x16_bf16, bf16")
+    print(json.dumps({
+        "metric": f"MFMA-only throughput, register operands ({name} operands from N(0,1))",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "frac_of_peak": round(tflops / peak, 4),
+        "peak": peak, "steps": args.steps, "warmup": args.warmup, "kernel_avg_ms": round(ms, 5),
+        "launch_ms": per_launch, "workgroups": wg, "waves_per_simd": 1,
+        "mfma_per_wave": mfmas_per_wave,
+        "cycles_per_mfma": round(float(np.median(cyc)) / mfmas_per_wave, 3),
+        "clock_mhz_measured": clock.result(), "peak_clock_mhz": caps.clock_khz // 1000,
+    }), flush=True)
 
 
 def torch_matmul_time(w, io, warmup, steps, stream):
@@ -359,28 +481,60 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, A, B, target_s):
-    """The oracle as it is, on this host's cores, over the first r rows."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_rate(w, A, B, target_s, n_threads):
+    """The oracle on the first r rows of C, r scaled so the run takes about
+    target_s seconds with n_threads threads (0: every thread OpenMP has)."""
     import oracle
-    threads = oracle.threads()
     a = A.reshape(w.M, w.K)
-    rows = max(1, min(w.M, 16))
+    rows = 1
     t0 = time.perf_counter()
-    oracle.gemm(a[:rows].contiguous(), B, rows, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue)
+    oracle.gemm(a[:rows].contiguous(), B, rows, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
+                n_threads=n_threads)
     dt = time.perf_counter() - t0
-    # scale to the target time, then measure that sample
+    if dt < 0.05:  # one row is too short to time: try 16
+        rows = min(w.M, 16)
+        t0 = time.perf_counter()
+        oracle.gemm(a[:rows].contiguous(), B, rows, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
+                    n_threads=n_threads)
+        dt = time.perf_counter() - t0
     rows = int(max(1, min(w.M, rows * target_s / max(dt, 1e-6))))
     t0 = time.perf_counter()
-    oracle.gemm(a[:rows].contiguous(), B, rows, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue)
+    oracle.gemm(a[:rows].contiguous(), B, rows, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
+                n_threads=n_threads)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
+    return flops / dt, rows, flops, dt
+
+
+def cpu_baseline(w, A, B, target_s):
+    """The oracle as it is, on this host's cores (all OpenMP threads, then
+    one), over the first r rows of C."""
+    import oracle
+    threads = oracle.threads()
+    rate, rows, flops, dt = oracle_rate(w, A, B, target_s, 0)
+    rate1, rows1, flops1, dt1 = oracle_rate(w, A, B, target_s * 0.5, 1)
     return {
-        "value": round(flops / dt / 1e12, 6),
+        "value": round(rate / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"first {rows} of {w.M} rows of C ({rows}x{w.N}x{w.K}, "
-                  f"{flops / 1e9:.1f} GFLOP) in {dt:.2f} s",
+                  f"{flops / 1e9:.1f} GFLOP) in {dt:.2f} s on {threads} threads",
+        "cpu_model": cpu_model(),
+        "logical_cpus": os.cpu_count(),
+        "single_core": {"value": round(rate1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                        "sample": f"first {rows1} rows ({flops1 / 1e9:.1f} GFLOP) in {dt1:.2f} s"},
     }
 
 

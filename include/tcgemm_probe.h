@@ -33,7 +33,8 @@ enum {
   TCG_PROBE_MFMA_32x32x16_BF16 = 0,
   TCG_PROBE_MFMA_32x32x16_F16 = 1,
   TCG_PROBE_MFMA_16x16x32_BF16 = 2,
-  TCG_PROBE_MFMA_16x16x32_F16 = 3
+  TCG_PROBE_MFMA_16x16x32_F16 = 3,
+  TCG_PROBE_MFMA_32x32x64_FP8 = 4 /* tcg_probe_mfma_rate only: f8f6f4, both operands E4M3, unscaled */
 };
 
 /*
@@ -87,6 +88,45 @@ int tcg_probe_mfma_f8(const uint8_t* a_regs_dev, const uint8_t* b_regs_dev, floa
  */
 int tcg_probe_ds_read_tr8(const uint8_t* lds_init_dev, int n_bytes, const uint32_t* lane_byte_addr_host,
                           uint8_t* out_dev, void* stream);
+
+/*
+ * Measurement probes (not layout probes): they launch many workgroups.
+ *
+ * tcg_probe_clock: `workgroups` workgroups of one wave; the first lane of
+ * workgroup g writes out_dev[3g] = the XCD it ran on (the XCC_ID hardware
+ * register), out_dev[3g+1] = the shader-clock counter (s_memtime) and
+ * out_dev[3g+2] = the constant-rate counter (s_memrealtime), whose rate
+ * tcg_probe_wallclock_khz reports.  out_dev holds 3 * workgroups values
+ * (device memory, caller-owned).  Two launches around a stretch of work on
+ * one stream give, per XCD, the average shader clock over that stretch
+ * (difference of s_memtime over difference of s_memrealtime, times the
+ * constant rate).  1 <= workgroups <= 65536, else GEMM_E_ARG.
+ */
+int tcg_probe_clock(int workgroups, uint64_t* out_dev, void* stream);
+
+/* The constant rate of s_memrealtime on `device`, in kHz (hipDeviceAttributeWallClockRate).
+ * Host only; GEMM_E_DEVICE if the runtime cannot report it. */
+int tcg_probe_wallclock_khz(int device, int* khz);
+
+/*
+ * Sustained MFMA throughput with operands in registers (no memory traffic
+ * inside the loop): `workgroups` workgroups of four waves, one wave per SIMD
+ * (each workgroup reserves 96 KiB of LDS, so at most one runs per CU).  Each
+ * wave loads 16 operand register sets of 8 16-bit values per lane from
+ * operands_dev ([16][64][8] values; for TCG_PROBE_MFMA_32x32x64_FP8, 32
+ * bytes per lane and set, [16][64][32] bytes: sets 0-7 are A, 8-15 are B; the
+ * caller draws them, e.g. Gaussian, since the clock under MFMA load depends
+ * on the operand bits), then runs `iters` rounds of 64 MFMAs of shape `kind`
+ * (TCG_PROBE_MFMA_*) into four independent accumulators, pairing A register
+ * i with B register (i + j) mod 8 in round j.  sink_dev receives one float
+ * per lane (workgroups * 256), so no MFMA is dead code; ticks_dev receives,
+ * per workgroup, the shader-clock cycles (s_memtime) of wave 0's loop.
+ * Flops per launch: workgroups * 4 * iters * 64 * (32768 for 32x32x16,
+ * 16384 for 16x16x32, 131072 for the FP8 32x32x64).  GEMM_E_ARG on a bad
+ * kind, count or null pointer.
+ */
+int tcg_probe_mfma_rate(int kind, int workgroups, int iters, const uint16_t* operands_dev, float* sink_dev,
+                        uint64_t* ticks_dev, void* stream);
 
 #ifdef __cplusplus
 }

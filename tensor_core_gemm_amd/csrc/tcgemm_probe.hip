@@ -123,6 +123,133 @@ __global__ __launch_bounds__(64) void probe_buffer_lds_kernel(const uint32_t* sr
   for (int i = threadIdx.x; i < kDmaLdsBytes / 4; i += 64) out[i] = lds[i];
 }
 
+// Clock probe: the first lane of each workgroup records which XCD it runs
+// on (the XCC_ID hardware register), the shader-clock counter (s_memtime)
+// and the constant-rate counter (s_memrealtime).  Two launches bracketing a
+// stretch of work give, per XCD, the average shader clock over it.
+__global__ __launch_bounds__(64) void probe_clock_kernel(uint64_t* out) {
+  if (threadIdx.x == 0) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    const uint64_t t = __builtin_amdgcn_s_memtime();
+    const uint64_t r = __builtin_amdgcn_s_memrealtime();
+    out[3 * blockIdx.x] = xcc & 0xffu;
+    out[3 * blockIdx.x + 1] = t;
+    out[3 * blockIdx.x + 2] = r;
+  }
+}
+
+// Sustained MFMA throughput with register operands: no memory traffic, no
+// LDS, no barriers inside the loop.  One workgroup of four waves per CU (one
+// wave per SIMD, as in the GEMM kernels; the workgroup's LDS reservation
+// keeps a second workgroup off the CU), each wave issuing back-to-back MFMAs
+// into four independent accumulators while it cycles through eight A and
+// eight B operand registers, pairing A register i with B register (i + j)
+// mod 8 in round j, so consecutive MFMAs see different values as in a GEMM
+// (the shader clock under this load depends on the operand bits).
+constexpr int kRateLdsBytes = 96 * 1024;
+
+template <int KIND>
+__device__ __forceinline__ void rate_mfma(const u32x4& a, const u32x4& b, f32x16& acc) {
+  if constexpr (KIND == TCG_PROBE_MFMA_32x32x16_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                  acc, 0, 0, 0);
+  } else if constexpr (KIND == TCG_PROBE_MFMA_32x32x16_F16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                 acc, 0, 0, 0);
+  } else {
+    // the 16x16x32 forms use the first four accumulator registers
+    f32x4 c = {acc[0], acc[1], acc[2], acc[3]};
+    if constexpr (KIND == TCG_PROBE_MFMA_16x16x32_BF16)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+    else
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                 0, 0);
+    acc[0] = c[0];
+    acc[1] = c[1];
+    acc[2] = c[2];
+    acc[3] = c[3];
+  }
+}
+
+// FP8 E4M3 operands: 32 bytes per lane per register set (8 words).
+__global__ __launch_bounds__(256) void probe_mfma_rate_f8_kernel(const uint32_t* ops, int iters, float* sink,
+                                                                 uint64_t* ticks) {
+  __shared__ char reserve[kRateLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (iters < 0) ((volatile char*)reserve)[tid] = 0;  // keeps the reservation; never taken
+  i32x8 a[8], b[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      a[r][q] = (int)ops[(r * 64 + lane) * 8 + q];
+      b[r][q] = (int)ops[((8 + r) * 64 + lane) * 8 + q];
+    }
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[i & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[(i + j) & 7], acc[i & 3], 0, 0, 0, 0,
+                                                                     0, 0);
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[blockIdx.x * 256 + tid] = s;
+  if (tid == 0) ticks[blockIdx.x] = t1 - t0;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void probe_mfma_rate_kernel(const uint16_t* ops, int iters, float* sink,
+                                                              uint64_t* ticks) {
+  __shared__ char reserve[kRateLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (iters < 0) ((volatile char*)reserve)[tid] = 0;  // keeps the reservation; never taken
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const uint16_t* pa = ops + (r * 64 + lane) * 8;
+    const uint16_t* pb = ops + ((8 + r) * 64 + lane) * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[r][q] = (uint32_t)pa[2 * q] | ((uint32_t)pa[2 * q + 1] << 16);
+      b[r][q] = (uint32_t)pb[2 * q] | ((uint32_t)pb[2 * q + 1] << 16);
+    }
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rate_mfma<KIND>(a[i], b[(i + j) & 7], acc[i & 3]);
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[blockIdx.x * 256 + tid] = s;
+  if (tid == 0) ticks[blockIdx.x] = t1 - t0;
+}
+
 int launch_status() { return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_E_LAUNCH; }
 
 }  // namespace
@@ -184,5 +311,52 @@ extern "C" int tcg_probe_ds_read_tr8(const uint8_t* lds_init_dev, int n_bytes, c
   }
   hipLaunchKernelGGL(probe_tr8_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, lds_init_dev, n_bytes, a,
                      out_dev);
+  return launch_status();
+}
+
+extern "C" int tcg_probe_clock(int workgroups, uint64_t* out_dev, void* stream) {
+  if (workgroups < 1 || workgroups > 65536 || !out_dev) return GEMM_E_ARG;
+  hipLaunchKernelGGL(probe_clock_kernel, dim3((uint32_t)workgroups), dim3(64), 0, (hipStream_t)stream, out_dev);
+  return launch_status();
+}
+
+extern "C" int tcg_probe_wallclock_khz(int device, int* khz) {
+  if (!khz) return GEMM_E_ARG;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, device) != hipSuccess) return GEMM_E_DEVICE;
+  *khz = v;
+  return GEMM_OK;
+}
+
+extern "C" int tcg_probe_mfma_rate(int kind, int workgroups, int iters, const uint16_t* operands_dev,
+                                   float* sink_dev, uint64_t* ticks_dev, void* stream) {
+  if (kind < 0 || kind > TCG_PROBE_MFMA_32x32x64_FP8 || workgroups < 1 || workgroups > 65536 || iters < 0 ||
+      !operands_dev ||
+      !sink_dev || !ticks_dev)
+    return GEMM_E_ARG;
+  const dim3 g((uint32_t)workgroups), b(256);
+  const hipStream_t s = (hipStream_t)stream;
+  switch (kind) {
+    case TCG_PROBE_MFMA_32x32x16_BF16:
+      hipLaunchKernelGGL(probe_mfma_rate_kernel<TCG_PROBE_MFMA_32x32x16_BF16>, g, b, 0, s, operands_dev, iters,
+                         sink_dev, ticks_dev);
+      break;
+    case TCG_PROBE_MFMA_32x32x16_F16:
+      hipLaunchKernelGGL(probe_mfma_rate_kernel<TCG_PROBE_MFMA_32x32x16_F16>, g, b, 0, s, operands_dev, iters,
+                         sink_dev, ticks_dev);
+      break;
+    case TCG_PROBE_MFMA_16x16x32_BF16:
+      hipLaunchKernelGGL(probe_mfma_rate_kernel<TCG_PROBE_MFMA_16x16x32_BF16>, g, b, 0, s, operands_dev, iters,
+                         sink_dev, ticks_dev);
+      break;
+    case TCG_PROBE_MFMA_16x16x32_F16:
+      hipLaunchKernelGGL(probe_mfma_rate_kernel<TCG_PROBE_MFMA_16x16x32_F16>, g, b, 0, s, operands_dev, iters,
+                         sink_dev, ticks_dev);
+      break;
+    default:
+      hipLaunchKernelGGL(probe_mfma_rate_f8_kernel, g, b, 0, s, (const uint32_t*)operands_dev, iters, sink_dev,
+                         ticks_dev);
+      break;
+  }
   return launch_status();
 }

@@ -9,6 +9,7 @@ import torch
 from ._lib import lib
 
 MFMA_32x32x16_BF16, MFMA_32x32x16_F16, MFMA_16x16x32_BF16, MFMA_16x16x32_F16 = 0, 1, 2, 3
+MFMA_32x32x64_FP8 = 4  # register-only rate probe only
 
 _vp = ctypes.c_void_p
 
@@ -87,3 +88,77 @@ def ds_read_tr8(lds_init: np.ndarray, lane_byte_addr: np.ndarray) -> np.ndarray:
            "tcg_probe_ds_read_tr8")
     torch.cuda.synchronize()
     return out.cpu().numpy().reshape(64, 8)
+
+
+# ---------------------------------------------------------------------------
+# Measurement probes: the shader clock and the register-only MFMA rate.
+
+def wallclock_khz(device: int = 0) -> int:
+    """Rate of the constant clock that s_memrealtime counts, in kHz."""
+    v = ctypes.c_int(0)
+    f = _fn("tcg_probe_wallclock_khz", [ctypes.c_int, ctypes.POINTER(ctypes.c_int)])
+    _check(f(device, ctypes.byref(v)), "tcg_probe_wallclock_khz")
+    return int(v.value)
+
+
+class ClockProbe:
+    """Average shader clock per XCD between two marks on one stream.
+
+    Each mark launches `workgroups` one-wave workgroups that record the XCD
+    they run on, the shader-clock counter and the constant-rate counter;
+    per XCD, the clock between the marks is the difference of the first
+    counter's medians over the difference of the second's, times the
+    constant rate."""
+
+    def __init__(self, workgroups: int = 2048, device: int = 0):
+        self.wg = workgroups
+        self.bufs = [torch.zeros(3 * workgroups, dtype=torch.int64, device="cuda") for _ in range(2)]
+        self.khz = wallclock_khz(device)
+        self._f = _fn("tcg_probe_clock", [ctypes.c_int, _vp, _vp])
+
+    def mark(self, which: int, stream=None):
+        s = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                            else torch.cuda.current_stream().cuda_stream)
+        _check(self._f(self.wg, self.bufs[which].data_ptr(), s), "tcg_probe_clock")
+
+    def result(self) -> dict:
+        """{'per_xcd_mhz': {xcd: MHz}, 'mean_mhz', 'min_mhz', 'max_mhz',
+        'seconds'} (call after both marks and a synchronisation)."""
+        a = self.bufs[0].cpu().numpy().reshape(-1, 3)
+        b = self.bufs[1].cpu().numpy().reshape(-1, 3)
+        per = {}
+        span = []
+        for x in sorted(set(a[:, 0].tolist()) & set(b[:, 0].tolist())):
+            ta, ra = a[a[:, 0] == x, 1], a[a[:, 0] == x, 2]
+            tb, rb = b[b[:, 0] == x, 1], b[b[:, 0] == x, 2]
+            dt = float(np.median(tb)) - float(np.median(ta))
+            dr = float(np.median(rb)) - float(np.median(ra))
+            if dr > 0:
+                per[int(x)] = round(dt / dr * self.khz / 1e3, 1)
+                span.append(dr / (self.khz * 1e3))
+        vals = list(per.values())
+        return {"per_xcd_mhz": per,
+                "mean_mhz": round(float(np.mean(vals)), 1) if vals else None,
+                "min_mhz": min(vals) if vals else None,
+                "max_mhz": max(vals) if vals else None,
+                "seconds": round(float(np.mean(span)), 6) if span else None}
+
+
+def mfma_rate(kind: int, workgroups: int, iters: int, operands: torch.Tensor, sink: torch.Tensor,
+              ticks: torch.Tensor, stream=None):
+    """One launch of the register-only MFMA loop (tcg_probe_mfma_rate):
+    operands is a device tensor of 16 * 64 * 16 bytes (16-bit kinds: 8
+    values per lane and register set) or 16 * 64 * 32 bytes (FP8), sink a
+    float32 tensor of workgroups * 256, ticks an int64 tensor of
+    workgroups.  Returns the flops the launch performs."""
+    need = 16 * 64 * (32 if kind == MFMA_32x32x64_FP8 else 16)
+    assert operands.is_cuda and operands.numel() * operands.element_size() >= need
+    assert sink.numel() >= workgroups * 256 and ticks.numel() >= workgroups
+    s = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                        else torch.cuda.current_stream().cuda_stream)
+    f = _fn("tcg_probe_mfma_rate", [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp])
+    _check(f(kind, workgroups, iters, operands.data_ptr(), sink.data_ptr(), ticks.data_ptr(), s),
+           "tcg_probe_mfma_rate")
+    per_mfma = {MFMA_32x32x16_BF16: 32768, MFMA_32x32x16_F16: 32768,
+                MFMA_32x32x64_FP8: 131072}.get(kind, 16384)
+    return workgroups * 4 * iters * 64 * per_mfma

@@ -221,3 +221,49 @@ def test_ds_read_tr8_permutation(probe):
             want_byte[j, e] = x % 8
     assert np.array_equal(lane_of.astype(np.int64), want_lane)
     assert np.array_equal(byte_of.astype(np.int64), want_byte)
+
+
+def test_clock_probe_reports_every_xcd_and_a_plausible_clock(probe):
+    """The clock probe: XCD ids within the device's count, both counters
+    advance between two marks, and over a stretch of back-to-back MFMA work
+    on every CU (no idle time between the marks: the shader-clock counter
+    slows down with the clock when the GPU idles) the clock lies between
+    500 MHz and the device's peak clock (plus margin)."""
+    import tensor_core_gemm_amd as tcg
+    caps = tcg.gemm_device_caps_query(0)
+    wg = caps.num_cus
+    ops = torch.zeros(16 * 64 * 8, dtype=torch.int16, device="cuda")
+    sink = torch.empty(wg * 256, device="cuda")
+    ticks = torch.zeros(wg, dtype=torch.int64, device="cuda")
+    cp = probe.ClockProbe(workgroups=1024)
+    torch.cuda.synchronize()
+    cp.mark(0)
+    for _ in range(20):
+        probe.mfma_rate(probe.MFMA_32x32x16_BF16, wg, 200, ops, sink, ticks)
+    cp.mark(1)
+    torch.cuda.synchronize()
+    a = cp.bufs[0].cpu().numpy().reshape(-1, 3)
+    assert set(a[:, 0].tolist()) <= set(range(max(caps.num_xcds, 1)))
+    r = cp.result()
+    print(f"clock probe: {r}", flush=True)
+    assert len(r["per_xcd_mhz"]) == max(caps.num_xcds, 1)
+    assert 500 <= r["min_mhz"] and r["max_mhz"] <= caps.clock_khz / 1000 * 1.1
+    assert r["seconds"] > 0
+
+
+def test_mfma_rate_probe_issues_back_to_back(probe):
+    """The register-only MFMA loop: every workgroup's loop takes about 32
+    shader cycles per v_mfma_f32_32x32x16_bf16 (8 passes of 4 cycles, the
+    rate the dense peak assumes), and its outputs are finite."""
+    wg, iters = 64, 10
+    gen = torch.Generator().manual_seed(3)
+    ops = (torch.randn(16 * 64 * 8, generator=gen) * 0.01).to(torch.bfloat16).view(torch.int16).cuda()
+    sink = torch.full((wg * 256,), float("nan"), device="cuda")
+    ticks = torch.zeros(wg, dtype=torch.int64, device="cuda")
+    flops = probe.mfma_rate(probe.MFMA_32x32x16_BF16, wg, iters, ops, sink, ticks)
+    torch.cuda.synchronize()
+    assert flops == wg * 4 * iters * 64 * 32768
+    assert torch.isfinite(sink).all()
+    cyc = ticks.cpu().numpy() / (iters * 64)
+    print(f"cycles per MFMA: median {np.median(cyc):.2f}", flush=True)
+    assert np.all(cyc >= 31.5) and np.median(cyc) <= 40
