@@ -313,7 +313,7 @@ extern "C" const char* gemm_strerror(int code) {
   switch (code) {
     case GEMM_OK: return "success";
     case GEMM_E_ARG: return "invalid argument (size, stride, flag, tile id or null pointer)";
-    case GEMM_E_DTYPE: return "unsupported storage type (inputs: F16 or BF16; output: F32, F16 or BF16)";
+    case GEMM_E_DTYPE: return "unsupported storage type (inputs: F16, BF16 or FP8 E4M3; output: F32, F16 or BF16)";
     case GEMM_E_ALIGN: return "pointer not aligned to its element size";
     case GEMM_E_ALIAS: return "C overlaps A or B (written parameters may not overlap others)";
     case GEMM_E_DEVICE: return "no usable gfx950 device, or the plan needs more LDS than it has";

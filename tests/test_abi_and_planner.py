@@ -36,9 +36,11 @@ def test_library_exports_every_declared_function():
 
 
 def test_strerror_names_every_code():
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         assert "unknown" not in tcg.gemm_strerror(code)
     assert "unknown" in tcg.gemm_strerror(-100)
+    # every input type the planner accepts is named
+    assert all(t in tcg.gemm_strerror(-2) for t in ("F16", "BF16", "FP8"))
 
 
 CAPS = tcg.make_caps()
