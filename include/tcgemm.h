@@ -121,8 +121,10 @@ enum {
   GEMM_E_NOMEM = -7,   /* host allocation of the plan failed                   */
   GEMM_E_PLAN = -8,    /* null or destroyed plan                               */
   GEMM_E_SIZE = -9,    /* a tile's byte offsets would not fit 31 bits          */
-  GEMM_E_WORKSPACE = -10 /* the plan needs a workspace (split K) and none, a
-                            smaller or a misaligned one was given             */
+  GEMM_E_WORKSPACE = -10, /* the plan needs a workspace (split K) and none, a
+                             smaller or a misaligned one was given            */
+  GEMM_E_SCRATCH = -11     /* gemm_run_noalloc: the plan's workspace is larger
+                             than GEMM_NOALLOC_SCRATCH_BYTES                  */
 };
 
 /* The problem.  M, N >= 0, K >= 0 (K == 0 gives C = epilogue(+0));
@@ -248,6 +250,29 @@ int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stre
  */
 int gemm_run_ex(gemm_plan_t plan, const void* A, const void* B, void* C, const gemm_run_args* args,
                 void* stream);
+
+/* Bytes of the fixed device array gemm_run_noalloc uses as its workspace
+ * (64 MiB: the four K ranges of a 2048 x 2048 fp32 output). */
+#define GEMM_NOALLOC_SCRATCH_BYTES (64ll << 20)
+
+/*
+ * gemm_run_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same run, with the optional bias (N fp32 values on the
+ * device, for plans made with GEMM_FLAG_BIAS, else ignored), where a
+ * split-K plan's workspace is a fixed array of GEMM_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends.
+ * The call allocates nothing: the array's device address is looked up
+ * (hipGetSymbolAddress) on the first call on each device and kept.
+ * Returns GEMM_E_SCRATCH, before touching the device, if the plan needs a
+ * larger workspace; otherwise what gemm_run_ex returns.  Every call on one
+ * GPU shares that GPU's array, which keeps the last call's partial sums:
+ * calls that overlap in time on one GPU (two streams, two host threads)
+ * race and may return wrong results, so serialise them.  Nothing in the
+ * array needs clearing between calls (every partial sum a run reads is
+ * written by that run first).
+ */
+int gemm_run_noalloc(gemm_plan_t plan, const void* A, const void* B, void* C, const void* bias, void* stream);
 
 /*
  * Measure and keep the fastest configuration for a problem (page

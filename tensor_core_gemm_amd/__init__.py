@@ -15,10 +15,10 @@ from .capi import (BF16, FP8, EPI_GELU, EPI_GELU_ERF, EPI_NONE, EPI_RELU, EPI_SI
                    FLAG_TUNED, FLAG_UNSTAGED, gemm_autotune, gemm_tune_cache_clear,
                    gemm_tune_cache_load, gemm_tune_cache_save, gemm_tune_cache_size, GEMM_E_ALIAS, GEMM_E_ALIGN, GEMM_E_ARG, GEMM_E_DEVICE,
                    GEMM_E_DTYPE, GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE,
-                   GEMM_E_WORKSPACE, GEMM_OK, CODE_TO_TORCH, TORCH_TO_CODE, GemmError, Plan,
+                   GEMM_E_WORKSPACE, GEMM_E_SCRATCH, NOALLOC_SCRATCH_BYTES, GEMM_OK, CODE_TO_TORCH, TORCH_TO_CODE, GemmError, Plan,
                    check_runtime, gemm_desc, gemm_device_caps, gemm_device_caps_query, gemm_plan,
                    gemm_plan_describe, gemm_plan_destroy, gemm_plan_for_caps, gemm_plan_get_info,
-                   gemm_plan_info, gemm_run, gemm_run_args, gemm_run_ex, gemm_runtime_version,
+                   gemm_plan_info, gemm_run, gemm_run_args, gemm_run_ex, gemm_run_noalloc, gemm_runtime_version,
                    gemm_stage_depth, gemm_strerror, gemm_tile_count, make_caps, make_desc)
 from ._lib import LIB_PATH, lib
 

@@ -21,7 +21,8 @@ FLAG_TUNED = 32
 GEMM_OK = 0
 GEMM_E_ARG, GEMM_E_DTYPE, GEMM_E_ALIGN, GEMM_E_ALIAS = -1, -2, -3, -4
 GEMM_E_DEVICE, GEMM_E_LAUNCH, GEMM_E_NOMEM, GEMM_E_PLAN, GEMM_E_SIZE = -5, -6, -7, -8, -9
-GEMM_E_WORKSPACE = -10
+GEMM_E_WORKSPACE, GEMM_E_SCRATCH = -10, -11
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GEMM_NOALLOC_SCRATCH_BYTES
 
 TORCH_TO_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
                  torch.float8_e4m3fn: FP8}
@@ -75,6 +76,7 @@ _SIGS = {
     "gemm_plan_describe": (ctypes.c_char_p, [_vp]),
     "gemm_run": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
     "gemm_run_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_void_p, _vp]),
+    "gemm_run_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "gemm_plan_destroy": (None, [_vp]),
     "gemm_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gemm_stage_depth": (ctypes.c_int, [ctypes.POINTER(gemm_device_caps), ctypes.c_int64,
@@ -238,6 +240,13 @@ def gemm_run_ex(plan: Plan, A, B, C, bias=None, workspace=None, workspace_bytes=
     args = gemm_run_args(_ptr(bias), _ptr(workspace), workspace_bytes)
     _check(_fn("gemm_run_ex")(plan.handle, _ptr(A), _ptr(B), _ptr(C), ctypes.byref(args),
                               _stream(stream)), "gemm_run_ex")
+
+
+def gemm_run_noalloc(plan: Plan, A, B, C, bias=None, stream=None) -> None:
+    """gemm_run_ex with the library's fixed device array as the split-K
+    workspace (no device allocation; calls that overlap on one GPU race)."""
+    _check(_fn("gemm_run_noalloc")(plan.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias),
+                                   _stream(stream)), "gemm_run_noalloc")
 
 
 def check_runtime() -> None:

@@ -322,6 +322,7 @@ extern "C" const char* gemm_strerror(int code) {
     case GEMM_E_PLAN: return "null or destroyed plan";
     case GEMM_E_SIZE: return "problem too large: a tile's byte offsets exceed 31 bits";
     case GEMM_E_WORKSPACE: return "the plan splits K and needs a larger or 256-byte aligned workspace";
+    case GEMM_E_SCRATCH: return "the plan needs a larger workspace than gemm_run_noalloc's fixed 64 MiB array";
     default: return "unknown error code";
   }
 }
