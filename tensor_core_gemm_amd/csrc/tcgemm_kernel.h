@@ -40,6 +40,7 @@
 
 #include "tcgemm_epilogue.h"
 #include "tcgemm_kernel_args.h"
+#include "tcgemm_layout.h"
 #include "tcgemm_tiles.h"
 
 namespace tcg {
@@ -63,47 +64,8 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr uint32_t kOOB = 0x80000000u;  // a byte offset no resource here reaches
 
-// ---------------------------------------------------------------------------
-// LDS layout: row-major slot, 16-byte chunks, chunk index XOR-swizzled by a
-// function of the row.  The XOR value stays below the row's power-of-two
-// chunk group, so the map is a bijection inside every row.  The functions
-// were chosen by measuring fragment-read throughput on gfx950 (whose LDS
-// serves 256-byte lines): for A's 16-byte row reads, the 16 rows that 16
-// lanes read must land on 16 different 16-byte bank groups; 16 / CPR rows
-// share a line, so the XOR follows r / (16 / CPR) (r/2 for 64-deep slots,
-// r/4 for 32-deep ones).  For B's transposing 8-byte reads, the four rows a
-// 16-lane group reads are spread by 2(r mod 4) chunks.
-template <int CPR>
-constexpr int swz_a_shift() {
-  return CPR >= 16 ? 0 : CPR >= 8 ? 1 : CPR >= 4 ? 2 : CPR >= 2 ? 3 : 4;
-}
-// Rows after which swz_a repeats.
-template <int CPR>
-constexpr int swz_a_period() {
-  return (1 << swz_a_shift<CPR>()) * (swizzle_mask(CPR) + 1);
-}
-template <int CPR>
-__device__ __forceinline__ int swz_a(int r) {
-  return (r >> swz_a_shift<CPR>()) & swizzle_mask(CPR);
-}
-// B with 16-bit elements: a transposing 8-byte read of 32 lanes covers 4
-// rows and 4 adjacent chunks of each (64 bytes), so where a row has 16
-// chunks or more the XOR 4(r mod 4) gives the 4 rows 4 different 64-byte
-// bank ranges; narrower rows keep 2(r mod 4).  B with 8-bit elements: a
-// read of 32 lanes covers 8 rows and two adjacent chunks of each, so the
-// XOR spreads 8 rows over 8 chunk pairs: 2(r mod 8).
-template <int CPR, int ES>
-__device__ __forceinline__ int swz_b(int r) {
-  if constexpr (ES == 2)
-    return (swizzle_mask(CPR) >= 15 ? 4 * (r & 3) : 2 * (r & 3)) & swizzle_mask(CPR);
-  else
-    return (2 * (r & 7)) & swizzle_mask(CPR);
-}
-// Rows after which swz_b repeats.
-template <int ES>
-constexpr int swz_b_period() {
-  return ES == 2 ? 4 : 8;
-}
+// The LDS layout (swizzles, copy plan, fragment-read addresses) is in
+// tcgemm_layout.h, shared with host-side checks.
 
 // ---------------------------------------------------------------------------
 // s_waitcnt immediate (gfx9 encoding): vmcnt = N (bits 3:0 and 15:14),
@@ -647,12 +609,12 @@ void gemm_kernel(KArgs a) {
                               (T::CH_A % NT == 0);
     constexpr bool SIMPLE_B = (NT % CPR_B == 0) && ((NT / CPR_B) % swz_b_period<ES>() == 0) && (T::CH_B % NT == 0);
     // Per-lane chunk of round 0 (rounds add NT / CPR rows).
-    const int a_r0 = tid / CPR_A;
-    const int a_c80 = EPC * ((tid % CPR_A) ^ swz_a<CPR_A>(a_r0));
-    const uint32_t a_off0 = (uint32_t)(a_r0 * K + a_c80) * ES;
-    const int b_r0 = tid / CPR_B;
-    const int b_c80 = EPC * ((tid % CPR_B) ^ swz_b<CPR_B, ES>(b_r0));
-    const uint32_t b_off0 = (uint32_t)(b_r0 * N + b_c80) * ES;
+    const ChunkRC a_ch0 = a_chunk_at<CPR_A>(tid);
+    const int a_c80 = EPC * a_ch0.c;
+    const uint32_t a_off0 = (uint32_t)(a_ch0.r * K + a_c80) * ES;
+    const ChunkRC b_ch0 = b_chunk_at<CPR_B, ES>(tid);
+    const int b_c80 = EPC * b_ch0.c;
+    const uint32_t b_off0 = (uint32_t)(b_ch0.r * N + b_c80) * ES;
     // Copy chunk (trip) t with element loads (rows not 16-byte aligned).
     auto copy_elements = [&](int t, lds_char* slot) __attribute__((always_inline)) {
       const int64_t k0 = kbase + (int64_t)t * BK;
@@ -661,9 +623,9 @@ void gemm_kernel(KArgs a) {
 #pragma unroll
       for (int i = 0; i < T::IA; ++i) {
         if (T::CH_A % NT == 0 || (i * NW + w) * 64 < T::CH_A) {
-          const int P = i * NT + tid;
-          const int r = P / CPR_A;
-          const int ce = EPC * ((P % CPR_A) ^ swz_a<CPR_A>(r));
+          const ChunkRC ch = a_chunk_at<CPR_A>(i * NT + tid);
+          const int r = ch.r;
+          const int ce = EPC * ch.c;
           const uint32_t off = (uint32_t)(r * K + ce) * ES;
           uint32_t e[EPC], wv[4];
 #pragma unroll
@@ -678,9 +640,9 @@ void gemm_kernel(KArgs a) {
 #pragma unroll
       for (int i = 0; i < T::IB; ++i) {
         if (T::CH_B % NT == 0 || (i * NW + w) * 64 < T::CH_B) {
-          const int P = i * NT + tid;
-          const int r = P / CPR_B;
-          const int ce = EPC * ((P % CPR_B) ^ swz_b<CPR_B, ES>(r));
+          const ChunkRC ch = b_chunk_at<CPR_B, ES>(i * NT + tid);
+          const int r = ch.r;
+          const int ce = EPC * ch.c;
           const uint32_t off = (uint32_t)(r * N + ce) * ES;
           uint32_t e[EPC], wv[4];
 #pragma unroll
@@ -718,10 +680,9 @@ void gemm_kernel(KArgs a) {
             c8 = a_c80;
             off = a_off0 + (uint32_t)(i * (NT / CPR_A) * K * ES);
           } else {
-            const int P = i * NT + tid;
-            const int r = P / CPR_A;
-            c8 = EPC * ((P % CPR_A) ^ swz_a<CPR_A>(r));
-            off = (uint32_t)(r * K + c8) * ES;
+            const ChunkRC ch = a_chunk_at<CPR_A>(i * NT + tid);
+            c8 = EPC * ch.c;
+            off = (uint32_t)(ch.r * K + c8) * ES;
           }
           lds_char* dst = slot + (i * NW + w) * 1024;
           const uint32_t o = (c.ktail && c.k0 + c8 >= K) ? kOOB : off;
@@ -736,10 +697,9 @@ void gemm_kernel(KArgs a) {
             c8 = b_c80;
             off = b_off0 + (uint32_t)(i * (NT / CPR_B) * N * ES);
           } else {
-            const int P = i * NT + tid;
-            const int r = P / CPR_B;
-            c8 = EPC * ((P % CPR_B) ^ swz_b<CPR_B, ES>(r));
-            off = (uint32_t)(r * N + c8) * ES;
+            const ChunkRC ch = b_chunk_at<CPR_B, ES>(i * NT + tid);
+            c8 = EPC * ch.c;
+            off = (uint32_t)(ch.r * N + c8) * ES;
           }
           lds_char* dst = slot + T::A_BYTES + (i * NW + w) * 1024;
           const uint32_t o = (b_ntail && col0 + c8 >= N) ? kOOB : off;
@@ -789,26 +749,13 @@ void gemm_kernel(KArgs a) {
     // b_base[j] + (64 s_k + 8t) * RB.
     constexpr int RA = BK * ES, RB = BN * ES;
     static_assert(32 % swz_a_period<CPR_A>() == 0, "A fragment rows must start on a swizzle period");
+    static_assert(RA == CPR_A * 16 && RB == CPR_B * 16, "row pitches are whole chunks");
     int a_base[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int r = wm0 + (lane & 31);
-      const int c = ES == 2 ? 2 * s + (lane >> 5) : 4 * s + 2 * (lane >> 5);
-      a_base[s] = r * RA + ((c ^ swz_a<CPR_A>(r)) * 16);
-    }
+    for (int s = 0; s < KS; ++s) a_base[s] = a_frag_base<CPR_A, ES>(lane, s, wm0);
     int b_base[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (ES == 2) {
-        const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
-        const int colq = wn0 + 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        b_base[j] = r * RB + (((colq >> 3) ^ swz_b<CPR_B, ES>(r)) * 16) + ((colq >> 2) & 1) * 8;
-      } else {
-        const int r = 32 * (lane >> 5) + ((lane & 15) >> 1);
-        const int colb = wn0 + 32 * j + 16 * ((lane >> 4) & 1);  // byte column of the 16-byte chunk
-        b_base[j] = r * RB + (((colb >> 4) ^ swz_b<CPR_B, ES>(r)) * 16) + (lane & 1) * 8;
-      }
-    }
+    for (int j = 0; j < FN; ++j) b_base[j] = b_frag_base<CPR_B, ES>(lane, j, wn0);
     struct Frags {
       frag_t a[FM], b[FN];
     };
@@ -826,12 +773,12 @@ void gemm_kernel(KArgs a) {
       } else {
         const int j = (r - RPA * FM) / RPB, h = (r - RPA * FM) % RPB;
         if constexpr (ES == 2) {
-          const lds_char* p = slot + T::A_BYTES + b_base[j] + (16 * s + 4 * h) * RB;
+          const lds_char* p = slot + T::A_BYTES + b_base[j] + b_frag_row<ES>(s, h) * RB;
           const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
           f.b[j][2 * h] = pack2((uint16_t)x[0], (uint16_t)x[1]);
           f.b[j][2 * h + 1] = pack2((uint16_t)x[2], (uint16_t)x[3]);
         } else {
-          const lds_char* p = slot + T::A_BYTES + b_base[j] + (64 * s + 8 * h) * RB;
+          const lds_char* p = slot + T::A_BYTES + b_base[j] + b_frag_row<ES>(s, h) * RB;
           const i32x2v x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
           f.b[j][2 * h] = (uint32_t)x[0];
           f.b[j][2 * h + 1] = (uint32_t)x[1];
