@@ -283,7 +283,10 @@ int gemm_run_noalloc(gemm_plan_t plan, const void* A, const void* B, void* C, co
  *
  * Candidates are every tile configuration (desc->tile == 0) or the one
  * given, each unsplit and, with GEMM_FLAG_SPLIT_K, split into 2, 4, 8 or 16
- * ranges of at least 4 trips where args->workspace holds the partial sums.
+ * ranges of at least 4 trips where args->workspace holds the partial sums;
+ * with GEMM_FLAG_SPLIT_K and desc->tile == 0 also the planner's own plan
+ * where it splits K for the bottom rows only (gemm_plan_info.tail_rows > 0)
+ * and the workspace holds its partial sums.
  * Each candidate runs once to warm up, then 5 times, each timed with HIP
  * events on `stream`; the smallest time wins.  A and B are read; C and the
  * workspace are written many times; the bias (GEMM_FLAG_BIAS) is read.
@@ -299,7 +302,8 @@ int gemm_autotune(const gemm_desc* desc, const void* A, const void* B, void* C, 
 
 /* The autotune cache as text, one problem per line (device key, problem
  * fields, chosen tile and split, measured microseconds): write it to
- * `path`, read entries from `path` (added to or replacing those held), or
+ * `path`, read entries from `path` (added to or replacing those held; a
+ * split of 0 stands for the planner's plan with its split tail), or
  * forget every entry.  Return GEMM_OK, or GEMM_E_ARG if the file cannot be
  * opened or a line does not parse. */
 int gemm_tune_cache_save(const char* path);

@@ -110,13 +110,18 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
             key = ("tuned", torch.cuda.current_device(), M, N, K, A.dtype, odt, epi, flags, batch)
             p = _plan_cache.get(key)
             if p is None:
-                tflags = flags | FLAG_SPLIT_K
-                wsb = min(16 * batch * M * N * 4, TUNE_WORKSPACE_CAP)  # sums of up to 16 ranges
-                ws = torch.empty(wsb, dtype=torch.uint8, device=A.device)
+                # Split candidates only where this run may split (not on a
+                # raw stream handle, where no workspace can be kept alive),
+                # so the tuner never keeps a plan the run below would refuse.
+                may_split = bool(flags & FLAG_SPLIT_K)
+                ws = None
+                if may_split:
+                    wsb = min(16 * batch * M * N * 4, TUNE_WORKSPACE_CAP)  # sums of up to 16 ranges
+                    ws = torch.empty(wsb, dtype=torch.uint8, device=A.device)
                 p = gemm_autotune(make_desc(M, N, K, TORCH_TO_CODE[A.dtype], TORCH_TO_CODE[odt], epi,
-                                            tflags, batch, *strides),
+                                            flags, batch, *strides),
                                   A, B, out, bias=bias, workspace=ws, stream=stream)
-                if stream is not None and not isinstance(stream, int):
+                if ws is not None and stream is not None and not isinstance(stream, int):
                     ws.record_stream(stream)
                 _plan_cache[key] = p
         else:

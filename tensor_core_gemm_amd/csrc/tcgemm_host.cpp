@@ -271,6 +271,9 @@ bool tail_choice(const gemm_desc& d, const gemm_device_caps& caps, int id, int64
 // Autotune cache: problem -> measured (tile, split).  The key is the
 // device's architecture and CU count and every field of the normalised
 // description but tile, split_k and GEMM_FLAG_TUNED.
+// A measured choice: a tile and a split of K into `split` ranges, or
+// split == 0 for the planner's own plan with its split tail (tile then
+// names the tile that plan runs).
 struct TuneChoice {
   int32_t tile;
   int32_t split;
@@ -480,10 +483,11 @@ extern "C" int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps*
   if (!caps || caps->num_cus <= 0 || caps->wave_size != 64) return GEMM_E_DEVICE;
   gemm_desc d = normalised(*desc);
   TuneChoice tc;
-  if ((d.flags & GEMM_FLAG_TUNED) && d.tile == 0 && d.split_k == 0 && tuned_choice(d, *caps, &tc)) {
+  if ((d.flags & GEMM_FLAG_TUNED) && d.tile == 0 && d.split_k == 0 && tuned_choice(d, *caps, &tc) &&
+      tc.split > 0) {
     d.tile = tc.tile;
     d.split_k = tc.split;
-  }
+  }  // (split 0: the planner's own plan with a split tail won; plan it again below)
   int id = 0;
   int64_t want_splits = 1;
   if (d.split_k > 0) {
@@ -814,6 +818,24 @@ extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B
   const int lo = base.tile ? base.tile : 1, hi = base.tile ? base.tile : tcg::kNumTiles;
   TuneChoice best{0, 1, 1e300};
   rc = GEMM_OK;
+  // One warm-up run, then the fastest of five timed runs of plan h (us), or
+  // an error code in *err.
+  auto time_plan = [&](gemm_plan_t h, int* err) {
+    double t_min = 1e300;
+    int r = gemm_run_ex(h, A, B, C, args, stream);  // warm-up
+    for (int rep = 0; rep < 5 && r == GEMM_OK; ++rep) {
+      float ms = 0.0f;
+      if (hipEventRecord(e0, s) != hipSuccess || (r = gemm_run_ex(h, A, B, C, args, stream)) != GEMM_OK ||
+          hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+          hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+        if (r == GEMM_OK) r = GEMM_E_LAUNCH;
+        break;
+      }
+      t_min = std::min(t_min, 1e3 * (double)ms);
+    }
+    *err = r;
+    return t_min;
+  };
   for (int id = lo; id <= hi && rc == GEMM_OK; ++id) {
     if (tcg::kTiles[id - 1].esize != in_size(base.in_dtype)) continue;  // built for the other width
     int last_split = 0;
@@ -833,18 +855,8 @@ extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B
         continue;
       }
       last_split = in.split_k;
-      double t_min = 1e300;
-      int r = gemm_run_ex(h, A, B, C, args, stream);  // warm-up
-      for (int rep = 0; rep < 5 && r == GEMM_OK; ++rep) {
-        float ms = 0.0f;
-        if (hipEventRecord(e0, s) != hipSuccess || (r = gemm_run_ex(h, A, B, C, args, stream)) != GEMM_OK ||
-            hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-            hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
-          if (r == GEMM_OK) r = GEMM_E_LAUNCH;
-          break;
-        }
-        t_min = std::min(t_min, 1e3 * (double)ms);
-      }
+      int r = GEMM_OK;
+      const double t_min = time_plan(h, &r);
       gemm_plan_destroy(h);
       if (r != GEMM_OK) {
         rc = r;
@@ -854,6 +866,26 @@ extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B
         std::fprintf(stderr, "[tcgemm] tune %lldx%lldx%lld: tile %d split %d: %.2f us\n", (long long)d.M,
                      (long long)d.N, (long long)d.K, id, sp, t_min);
       if (t_min < best.us) best = TuneChoice{id, sp, t_min};
+    }
+  }
+  // The planner's own plan where it splits K for the bottom rows only (a
+  // small last round of tiles): a candidate of its own, kept as split 0.
+  if (rc == GEMM_OK && base.tile == 0 && base.split_k == 0 && (base.flags & GEMM_FLAG_SPLIT_K)) {
+    gemm_desc d = base;
+    d.flags &= ~GEMM_FLAG_TUNED;
+    gemm_plan_t h = nullptr;
+    if (gemm_plan_for_caps(&d, &caps, &h) == GEMM_OK) {
+      const gemm_plan_info& in = reinterpret_cast<Plan*>(h)->info;
+      if (in.tail_rows > 0 && in.workspace_bytes <= ws_have) {
+        int r = GEMM_OK;
+        const double t_min = time_plan(h, &r);
+        if (r != GEMM_OK) rc = r;
+        if (r == GEMM_OK && log_enabled())
+          std::fprintf(stderr, "[tcgemm] tune %lldx%lldx%lld: planner's split tail (tile %d): %.2f us\n",
+                       (long long)d.M, (long long)d.N, (long long)d.K, in.tile_id, t_min);
+        if (r == GEMM_OK && t_min < best.us) best = TuneChoice{in.tile_id, 0, t_min};
+      }
+      gemm_plan_destroy(h);
     }
   }
   (void)hipEventDestroy(e0);
@@ -866,8 +898,10 @@ extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B
     g_tune[tune_key(base, caps)] = best;
   }
   gemm_desc d = base;
-  d.tile = best.tile;
-  d.split_k = best.split;
+  if (best.split > 0) {
+    d.tile = best.tile;
+    d.split_k = best.split;
+  }  // else the planner's own plan (its split tail)
   d.flags &= ~GEMM_FLAG_TUNED;
   return gemm_plan_for_caps(&d, &caps, out);
 }
@@ -896,7 +930,7 @@ extern "C" int gemm_tune_cache_load(const char* path) {
     double us;
     if (std::sscanf(line, "%63s %d %lld %lld %lld %d %d %d %d %lld %lld %lld %lld %d %d %lf", arch, &cus, &M, &N,
                     &K, &in, &o, &epi, &flags, &batch, &sa, &sb, &sc, &tile, &split, &us) != 16 ||
-        tile < 1 || tile > tcg::kNumTiles || split < 1 || split > kMaxSplits) {
+        tile < 1 || tile > tcg::kNumTiles || split < 0 || split > kMaxSplits) {
       rc = GEMM_E_ARG;
       break;
     }

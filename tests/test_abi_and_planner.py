@@ -396,3 +396,25 @@ def test_tune_cache_file_round_trip_and_tuned_plans(tmp_path):
     with pytest.raises(tcg.GemmError):
         tcg.gemm_tune_cache_load(str(tmp_path / "missing.txt"))
     tcg.gemm_tune_cache_clear()
+
+
+def test_tuned_split_tail_entry_replays_the_planners_tail_plan(tmp_path):
+    """A cache entry with split 0 stands for the planner's own plan with its
+    split tail (the autotuner's extra candidate): gemm_plan with
+    GEMM_FLAG_TUNED then returns that plan, tail included."""
+    tcg.gemm_tune_cache_clear()
+    M = N = K = 4608
+    ref = plan(M, N, K, flags=tcg.FLAG_SPLIT_K).info()
+    assert ref.tail_rows > 0  # this shape's last round of tiles is small
+    arch = CAPS.arch.decode()
+    line = (f"{arch} 256 {M} {N} {K} {BF16} {BF16} {EPI_RELU} {tcg.FLAG_SPLIT_K} 1 {M*K} {K*N} "
+            f"{M*N} {ref.tile_id} 0 171.0\n")
+    f = tmp_path / "tail.txt"
+    f.write_text(line)
+    tcg.gemm_tune_cache_load(str(f))
+    i = plan(M, N, K, flags=tcg.FLAG_SPLIT_K | tcg.FLAG_TUNED).info()
+    assert (i.tile_id, i.tail_rows, i.tail_split) == (ref.tile_id, ref.tail_rows, ref.tail_split)
+    g = tmp_path / "saved.txt"
+    tcg.gemm_tune_cache_save(str(g))
+    assert g.read_text().split()[13:15] == [str(ref.tile_id), "0"]
+    tcg.gemm_tune_cache_clear()

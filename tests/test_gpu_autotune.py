@@ -81,3 +81,53 @@ def test_matmul_tune_within_tolerance(tcg):
     assert np.array_equal(as_bits(C.cpu()), as_bits(C2.cpu()))
     check_against_oracle(w, A, B, C.cpu().reshape(1, w.M, w.N))
     tcg.gemm_tune_cache_clear()
+
+
+def test_matmul_tune_on_a_raw_stream_never_keeps_a_split_plan(tcg):
+    """On a raw stream handle no workspace can be kept alive, so the run
+    cannot split K; tune=True there must tune among unsplit plans only and
+    run, on the first call and on the cached plan (a long-K, few-tile shape
+    where splits would otherwise be candidates)."""
+    tcg.gemm_tune_cache_clear()
+    w = gw.custom(256, 512, 8192, BF16, F32, EPI_NONE, gw.INT4, seed=93)
+    A, B = gw.make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    raw = torch.cuda.current_stream().cuda_stream
+    note("matmul tune=True on a raw stream, 256x512x8192")
+    C1 = tcg.matmul(Ad, Bd, out_dtype=torch.float32, tune=True, stream=raw)
+    C2 = tcg.matmul(Ad, Bd, out_dtype=torch.float32, tune=True, stream=raw)
+    torch.cuda.synchronize()
+    check_against_oracle(w, A, B, C1.cpu().reshape(1, w.M, w.N))
+    assert np.array_equal(as_bits(C1.cpu()), as_bits(C2.cpu()))
+    tcg.gemm_tune_cache_clear()
+
+
+def test_autotune_considers_the_planners_split_tail(tcg):
+    """4608^3 with split K allowed: the planner's own plan splits K for its
+    last rows only; the autotuner times it with the tile candidates, and
+    whatever wins is exact on integer inputs and replayed by
+    GEMM_FLAG_TUNED (split 0 in the cache stands for the tail plan)."""
+    tcg.gemm_tune_cache_clear()
+    M = N = K = 4608
+    w = gw.custom(M, N, K, BF16, F32, EPI_RELU, gw.INT4, seed=94)
+    A, B = gw.make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    desc = tcg.make_desc(M, N, K, BF16, F32, EPI_RELU, tcg.FLAG_SPLIT_K)
+    planner = tcg.gemm_plan(desc).info()
+    assert planner.tail_rows > 0
+    ws = torch.empty(max(planner.workspace_bytes, 16 * M * N * 4) // 4, dtype=torch.float32,
+                     device="cuda")
+    p = tcg.gemm_autotune(desc, Ad, Bd, C, workspace=ws)
+    i = p.info()
+    note(f"4608^3 tuned: {p.describe()}")
+    q = tcg.gemm_plan(tcg.make_desc(M, N, K, BF16, F32, EPI_RELU,
+                                    tcg.FLAG_SPLIT_K | tcg.FLAG_TUNED)).info()
+    assert (q.tile_id, q.split_k, q.tail_rows) == (i.tile_id, i.split_k, i.tail_rows)
+    C.fill_(float("nan"))
+    tcg.gemm_run_ex(p, Ad, Bd, C, workspace=ws)
+    torch.cuda.synchronize()
+    bi, ii, jj = gw.sample_indices(M, N, 4096, 95)
+    want, _ = oracle.gemm_sampled(A, B, M, N, K, BF16, F32, EPI_RELU, bi, ii, jj)
+    assert np.array_equal(C.cpu().numpy()[ii, jj], want)
+    tcg.gemm_tune_cache_clear()
