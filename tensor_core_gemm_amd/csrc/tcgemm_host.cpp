@@ -69,12 +69,37 @@ int cached_caps(int device, gemm_device_caps* out) {
 
 bool is_gfx950(const gemm_device_caps& c) { return std::strncmp(c.arch, "gfx950", 6) == 0; }
 
+// Largest byte extent of one operand over all its batch items.  Every size
+// the host derives (extents, offsets, workspaces of up to kMaxSplits ranges,
+// grid sizes) stays far inside int64 below it, so no size arithmetic
+// overflows; 2^52 bytes is beyond any device's memory.
+constexpr int64_t kMaxExtentBytes = (int64_t)1 << 52;
+
+// Bytes spanned by `batch` items of rows x cols elements, `stride` elements
+// apart, or -1 if that is not below kMaxExtentBytes.
+int64_t extent_bytes(int64_t batch, int64_t stride, int64_t rows, int64_t cols, int64_t esize) {
+  int64_t item = 0, span = 0, total = 0, bytes = 0;
+  if (__builtin_mul_overflow(rows, cols, &item) || __builtin_mul_overflow(batch - 1, stride, &span) ||
+      __builtin_add_overflow(item, span, &total) || __builtin_mul_overflow(total, esize, &bytes) ||
+      bytes >= kMaxExtentBytes)
+    return -1;
+  return bytes;
+}
+
 int validate_desc(const gemm_desc* d) {
   if (!d) return GEMM_E_ARG;
   if (d->M < 0 || d->N < 0 || d->K < 0 || d->batch < 1) return GEMM_E_ARG;
   if (d->in_dtype != GEMM_F16 && d->in_dtype != GEMM_BF16 && d->in_dtype != GEMM_FP8) return GEMM_E_DTYPE;
   if (d->out_dtype != GEMM_F32 && d->out_dtype != GEMM_F16 && d->out_dtype != GEMM_BF16)
     return GEMM_E_DTYPE;
+  // Each operand's extent, with the strides a run will use (one item: none).
+  const int64_t sa = d->batch > 1 ? d->stride_a : 0, sb = d->batch > 1 ? d->stride_b : 0,
+                sc = d->batch > 1 ? d->stride_c : 0;
+  if (d->batch > 1 && (sa < 0 || sb < 0 || sc < 0)) return GEMM_E_ARG;
+  if (extent_bytes(d->batch, sa, d->M, d->K, in_size(d->in_dtype)) < 0 ||
+      extent_bytes(d->batch, sb, d->K, d->N, in_size(d->in_dtype)) < 0 ||
+      extent_bytes(d->batch, sc, d->M, d->N, 4) < 0)
+    return GEMM_E_SIZE;
   if (d->epilogue < GEMM_EPI_NONE || d->epilogue > GEMM_EPI_TANH) return GEMM_E_ARG;
   if (d->flags & ~(GEMM_FLAG_FORCE_STAGES_1 | GEMM_FLAG_UNSTAGED | GEMM_FLAG_FORCE_STAGES_2 |
                    GEMM_FLAG_BIAS | GEMM_FLAG_SPLIT_K | GEMM_FLAG_TUNED))
@@ -141,17 +166,17 @@ double estimate_us(const gemm_desc& d, const gemm_device_caps& caps, int id, int
   const int64_t slots = cus * c.per_cu;
   const double mn = (double)d.M * (double)d.N * (double)d.batch;
   double us = kFixedUs + mn * out_size(d.out_dtype) / kStoreBytesPerUs;
-  for (int64_t left = wgs; left > 0; left -= slots) {
-    const int64_t w = std::min(left, slots);
-    double trip;
-    if (w > cus)
-      trip = c.trip_shared;
-    else if (c.power_scaled)
-      trip = c.trip_alone + (c.trip_shared - c.trip_alone) * (double)w / (double)cus;
-    else
-      trip = c.trip_alone;
-    us += (double)tps * trip;
-  }
+  // Rounds of `slots` workgroups, then a last round of the rest; a round of
+  // w workgroups costs tps trips at the price for w (closed form: the
+  // number of rounds can be huge).
+  auto trip_cost = [&](int64_t w) {
+    if (w > cus) return c.trip_shared;
+    if (c.power_scaled) return c.trip_alone + (c.trip_shared - c.trip_alone) * (double)w / (double)cus;
+    return c.trip_alone;
+  };
+  const int64_t full = wgs / slots, rest = wgs % slots;
+  us += (double)full * (double)tps * trip_cost(slots);
+  if (rest > 0) us += (double)tps * trip_cost(rest);
   if (ranges > 1) us += (2.0 * ranges * mn * 4.0 + mn * out_size(d.out_dtype)) / kReduceBytesPerUs + kLaunchUs;
   return us;
 }
