@@ -195,20 +195,42 @@ typedef struct gemm_plan_info {
 
 typedef struct gemm_plan_s* gemm_plan_t;
 
-/* Device capabilities of HIP device `device` (host call; no kernel). */
+/* Device capabilities of HIP device `device` (host call; no kernel): what the
+ * stage rule and the tile choice read about a target (page "Module
+ * Tolk.Stage": Renderer.t.async_copy, Renderer.t.shared_max).  Returns
+ * GEMM_E_DEVICE, with *out filled as far as known, if the device does not
+ * exist or is not a gfx950; GEMM_E_ARG if out is NULL. */
 int gemm_device_caps_query(int device, gemm_device_caps* out);
 
-/* Plan for the current HIP device (queries it once per device). */
+/* Plan for the current HIP device (queries it once per device): the
+ * decisions a lowering makes before any launch -- the tile and its wave
+ * grid, the number of LDS stages (page "Module Tolk.Stage", depth), the K
+ * split, and the grid of ceil(M / BM) x ceil(N / BN) x batch x split_k
+ * workgroups (page "gizml:tile", cdiv; the tile program's launch grid).
+ * The page's `ir` and `source` likewise fix these per kind and arch with
+ * no launch.  Host only: no GPU work, no device memory.  *out receives a new
+ * plan the caller owns (gemm_plan_destroy), or NULL on error: GEMM_E_ARG,
+ * GEMM_E_DTYPE or GEMM_E_SIZE for a bad description, GEMM_E_DEVICE if the
+ * current device is not a gfx950 or no tile fits it, GEMM_E_NOMEM. */
 int gemm_plan(const gemm_desc* desc, gemm_plan_t* out);
 
-/* Plan for the given capabilities: host only, no device needed. */
+/* gemm_plan for the given capabilities instead of the current device: no
+ * device needed (as the page "gizml:tile", source, lowers for a named
+ * kind and arch "with no GPU needed").  Same ownership and errors as
+ * gemm_plan; GEMM_E_DEVICE if caps is NULL or not a 64-lane device. */
 int gemm_plan_for_caps(const gemm_desc* desc, const gemm_device_caps* caps, gemm_plan_t* out);
 
-/* Copy a plan's decisions out. */
+/* Copy a plan's decisions out (the fields the page "gizml:tile", ir,
+ * reports per node: shape, storage, the mma warp layout).  GEMM_E_PLAN for
+ * a NULL plan or a pointer that is not a plan, GEMM_E_ARG if out is NULL. */
 int gemm_plan_get_info(gemm_plan_t plan, gemm_plan_info* out);
 
-/* A one-line description (tile, stages, LDS bytes, grid, MFMA shape); the
- * string belongs to the plan. */
+/* A one-line description (tile, stages, LDS bytes, grid, MFMA shape): the
+ * counterpart of the page "gizml:tile", ir (the lowering's decisions as
+ * text, the first thing to read when a launch is slower than expected).
+ * The string belongs to the plan and lives until gemm_plan_destroy; a NULL
+ * plan (or a pointer that is not a plan) gives the static text
+ * "(invalid plan)". */
 const char* gemm_plan_describe(gemm_plan_t plan);
 
 /* Extra arguments of a run.  bias: device pointer to N fp32 values, needed
@@ -226,7 +248,9 @@ typedef struct gemm_run_args {
 
 /*
  * Launch C = epilogue(A . B) on `stream` (a hipStream_t; NULL = the null
- * stream).  A, B, C are device pointers owned by the caller, aligned to
+ * stream): the page "gizml:tile", run (the body runs for each point of the
+ * grid; the written tensor keeps its values outside what the programs
+ * store, Out.put).  A, B, C are device pointers owned by the caller, aligned to
  * their element size; 16-byte-aligned A and B with K and N multiples of 8
  * (16 for FP8: whole 16-byte chunks)
  * take the 16-byte copy path, others take the element path (same bits).
@@ -238,8 +262,9 @@ typedef struct gemm_run_args {
 int gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream);
 
 /*
- * gemm_run with a bias and a workspace (args may be NULL for plans that
- * need neither).  A split-K plan launches two kernels on `stream`: the GEMM,
+ * gemm_run with a bias (page "gizml:tile", Tile.add with a [1, N] row
+ * broadcast) and a workspace (args may be NULL for plans that need
+ * neither).  A split-K plan launches two kernels on `stream`: the GEMM,
  * which writes each K range's fp32 sums into the workspace, then the
  * reduction, which writes C.  Returns GEMM_E_ARG if the plan needs a bias
  * and none is given (or args->reserved is not 0), GEMM_E_WORKSPACE if it
@@ -312,10 +337,17 @@ void gemm_tune_cache_clear(void);
 /* Number of entries held. */
 int gemm_tune_cache_size(void);
 
-/* Free a plan (NULL is ignored). */
+/* Free a plan (NULL is ignored).  A plan is the host-side record of one
+ * lowering (page "gizml:tile": a tile program's body runs once and records
+ * its IR; here that record is host memory the caller owns).  Runs already
+ * queued with it are unaffected (they copied its decisions at launch); the
+ * plan may not be used afterwards (a freed plan cannot be detected: no
+ * call promises an error for one). */
 void gemm_plan_destroy(gemm_plan_t plan);
 
-/* Static text naming an error code. */
+/* Static text naming an error code: failures are named and specific (page
+ * "Module Tolk.Uniform", check: the error names the kernel, the operation
+ * and the loop).  Unknown codes give "unknown error code". */
 const char* gemm_strerror(int code);
 
 /*
@@ -329,10 +361,14 @@ const char* gemm_strerror(int code);
 int gemm_stage_depth(const gemm_device_caps* caps, int64_t used, const int64_t* tile_bytes,
                      int n_tiles, int stage_enabled);
 
-/* Number of tile configurations (valid `tile` ids are 1 .. count). */
+/* Number of tile configurations (valid `tile` ids are 1 .. count): the
+ * configurations a tuned launch chooses among (page "gizml:tile", tune). */
 int gemm_tile_count(void);
 
-/* HIP runtime version the library is running against (hipRuntimeGetVersion). */
+/* HIP runtime version the library is running against (hipRuntimeGetVersion),
+ * or -1.  A diagnostic of this build with no counterpart on the pages: a
+ * process must run the library on the runtime its caller's device pointers
+ * and streams come from. */
 int gemm_runtime_version(void);
 
 #ifdef __cplusplus
