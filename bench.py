@@ -86,6 +86,9 @@ def parse():
                          "with E4M3 operands)")
     ap.add_argument("--ceiling-iters", type=int, default=0,
                     help="rounds of 64 MFMAs per wave in one --mfma-ceiling launch")
+    ap.add_argument("--copy-issue-cost", action="store_true",
+                    help="instead of the GEMM: MFMA loops with global->LDS copies in between "
+                         "(tcg_probe_copy_issue), cycles per MFMA per SIMD for each pattern")
     ap.add_argument("--planner-sweep", action="store_true",
                     help="instead of the bench line: for a sweep of bf16 relu shapes, time the "
                          "planner's choice, the autotuner's and torch.matmul (one JSON line each)")
@@ -170,6 +173,9 @@ def main():
         return
     if args.mfma_ceiling:
         mfma_ceiling(args)
+        return
+    if args.copy_issue_cost:
+        copy_issue_cost()
         return
     w = gw.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -404,6 +410,37 @@ def mfma_ceiling(args):
         "cycles_per_mfma": round(float(np.median(cyc)) / mfmas_per_wave, 3),
         "clock_mhz_measured": clock.result(), "peak_clock_mhz": caps.clock_khz // 1000,
     }), flush=True)
+
+
+def copy_issue_cost():
+    """Cycles per MFMA per SIMD of a register-only MFMA loop with and without
+    global->LDS copies between the MFMAs, with one and two waves per SIMD
+    (tcg_probe_copy_issue; median over the CUs, after 100 warm-up launches)."""
+    import numpy as np
+    import torch
+
+    import gemm_workloads as gw
+    import tensor_core_gemm_amd as tcg
+    from tensor_core_gemm_amd import probe
+
+    wg = tcg.gemm_device_caps_query(0).num_cus
+    gen = torch.Generator().manual_seed(11)
+    ops = gw.draw((8 * 64 * 8,), gw.NORMAL, gw.BF16, gen).view(torch.int16).cuda()
+    src = torch.zeros(65536 // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(wg * 512, device="cuda")
+    ticks = torch.zeros(wg, dtype=torch.int64, device="cuda")
+    iters = 400
+    out = {}
+    for pat, (name, _) in probe.COPY_PATTERNS.items():
+        for _ in range(100):
+            per_simd = probe.copy_issue(pat, wg, iters, ops, src, sink, ticks)
+        torch.cuda.synchronize()
+        cyc = ticks.cpu().numpy().astype(np.float64) / per_simd
+        out[name] = round(float(np.median(cyc)), 2)
+    print(json.dumps({"metric": "cycles per MFMA per SIMD (v_mfma_f32_32x32x16_bf16, register operands), "
+                                "with global->LDS copies between the MFMAs",
+                      "mfmas_per_round_per_wave": 32, "rounds": iters, "workgroups": wg,
+                      "patterns": out}), flush=True)
 
 
 def torch_matmul_time(w, io, warmup, steps, stream):

@@ -19,6 +19,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 
@@ -250,6 +251,85 @@ __global__ __launch_bounds__(256) void probe_mfma_rate_kernel(const uint16_t* op
   if (tid == 0) ticks[blockIdx.x] = t1 - t0;
 }
 
+// Issue cost of global->LDS copies between MFMAs.  One workgroup per CU
+// (each reserves 96 KiB of LDS) of NWV waves; every wave runs `iters`
+// rounds of 32 back-to-back v_mfma_f32_32x32x16_bf16 on register operands
+// (four accumulators), and issues NB bursts of BURST 16-byte-per-lane
+// copies into LDS per round, each burst right after an MFMA, bursts evenly
+// spaced.  The copies read a 64 KiB buffer (offsets below 64 KiB - 16) and
+// write this workgroup's LDS (wave w: 8 KiB at 8 KiB w); a wait for all but
+// the last 15 copies closes each round.  The loop is timed with s_memtime
+// between two workgroup barriers, so it covers every wave.  Compared with
+// the copy-free loop, the time per MFMA shows how long a copy holds up the
+// MFMA issue of its wave, and how much a second wave on the SIMD hides.
+constexpr int kCopyProbeLds = 96 * 1024;
+
+template <int NWV, int NB, int BURST>
+__global__ __launch_bounds__(NWV * 64) void probe_copy_issue_kernel(const uint16_t* ops, const uint32_t* src,
+                                                                   int iters, float* sink, uint64_t* ticks) {
+  __shared__ __attribute__((aligned(1024))) char lds[kCopyProbeLds];
+  constexpr int RM = 32;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  u32x4 a[4], b[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[r][q] = (uint32_t)ops[(r * 64 + lane) * 8 + 2 * q] | ((uint32_t)ops[(r * 64 + lane) * 8 + 2 * q + 1] << 16);
+      b[r][q] = (uint32_t)ops[((4 + r) * 64 + lane) * 8 + 2 * q] |
+                ((uint32_t)ops[((4 + r) * 64 + lane) * 8 + 2 * q + 1] << 16);
+    }
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  i32x4 rs;
+  {
+    const uint64_t base = (uint64_t)src;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)((base >> 32) & 0xffffu));
+    rs[2] = 65536;
+    rs[3] = 0x00020000;
+  }
+  const uint32_t voff = (uint32_t)(lane * 16 + (w & 3) * 1024);  // + k * 4096 < 65536 - 16
+  const uint32_t ldsb = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds + w * 8192;
+  constexpr int SP = NB > 0 ? RM / NB : RM;
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[m & 3]),
+                                                           __builtin_bit_cast(bf16x8, b[(m >> 2) & 3]), acc[m & 3], 0,
+                                                           0, 0);
+      if (NB > 0 && (m % SP) == SP - 1) {
+#pragma unroll
+        for (int q = 0; q < BURST; ++q) {
+          const int k = ((m / SP) * BURST + q) & 7;  // 8 x 1 KiB of LDS per wave
+          const uint32_t m0 = __builtin_amdgcn_readfirstlane(ldsb + k * 1024);
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       :
+                       : "s"(m0), "v"(voff + k * 4096), "s"(rs)
+                       : "memory", "m0");
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NB > 0) __builtin_amdgcn_s_waitcnt(0xF7F);  // vmcnt(15)
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[blockIdx.x * 512 + tid] = s + (float)lds[tid];
+  if (tid == 0) ticks[blockIdx.x] = t1 - t0;
+}
+
 int launch_status() { return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_E_LAUNCH; }
 
 }  // namespace
@@ -358,5 +438,30 @@ extern "C" int tcg_probe_mfma_rate(int kind, int workgroups, int iters, const ui
                          ticks_dev);
       break;
   }
+  return launch_status();
+}
+
+extern "C" int tcg_probe_copy_issue(int pattern, int workgroups, int iters, const uint16_t* operands_dev,
+                                    const uint32_t* src_dev, float* sink_dev, uint64_t* ticks_dev, void* stream) {
+  if (workgroups < 1 || workgroups > 65536 || iters < 0 || !operands_dev || !src_dev || !sink_dev || !ticks_dev)
+    return GEMM_E_ARG;
+  const dim3 g((uint32_t)workgroups);
+  const hipStream_t s = (hipStream_t)stream;
+#define TCG_COPY_CASE(P, NWV, NB, BURST)                                                                  \
+  case P:                                                                                                 \
+    hipLaunchKernelGGL((probe_copy_issue_kernel<NWV, NB, BURST>), g, dim3(NWV * 64), 0, s, operands_dev, src_dev, \
+                       iters, sink_dev, ticks_dev);                                                       \
+    break;
+  switch (pattern) {
+    TCG_COPY_CASE(TCG_PROBE_COPY_4W_NONE, 4, 0, 0)
+    TCG_COPY_CASE(TCG_PROBE_COPY_4W_8X1, 4, 8, 1)
+    TCG_COPY_CASE(TCG_PROBE_COPY_4W_2X4, 4, 2, 4)
+    TCG_COPY_CASE(TCG_PROBE_COPY_8W_NONE, 8, 0, 0)
+    TCG_COPY_CASE(TCG_PROBE_COPY_8W_4X1, 8, 4, 1)
+    TCG_COPY_CASE(TCG_PROBE_COPY_8W_8X1, 8, 8, 1)
+    default:
+      return GEMM_E_ARG;
+  }
+#undef TCG_COPY_CASE
   return launch_status();
 }

@@ -162,3 +162,24 @@ def mfma_rate(kind: int, workgroups: int, iters: int, operands: torch.Tensor, si
     per_mfma = {MFMA_32x32x16_BF16: 32768, MFMA_32x32x16_F16: 32768,
                 MFMA_32x32x64_FP8: 131072}.get(kind, 16384)
     return workgroups * 4 * iters * 64 * per_mfma
+
+
+COPY_PATTERNS = {0: ("4 waves, no copies", 4), 1: ("4 waves, 8 copies, 1 per 4 MFMAs", 4),
+                 2: ("4 waves, 8 copies, 2 bursts of 4", 4), 3: ("8 waves, no copies", 8),
+                 4: ("8 waves, 4 copies each (same per SIMD as 1)", 8),
+                 5: ("8 waves, 8 copies each (twice 1 per SIMD)", 8)}
+
+
+def copy_issue(pattern: int, workgroups: int, iters: int, operands: torch.Tensor, src: torch.Tensor,
+               sink: torch.Tensor, ticks: torch.Tensor, stream=None):
+    """One launch of tcg_probe_copy_issue; returns the MFMAs one SIMD issues
+    (for cycles per MFMA per SIMD = ticks / that)."""
+    assert operands.is_cuda and operands.numel() * operands.element_size() >= 8 * 64 * 8 * 2
+    assert src.is_cuda and src.numel() * src.element_size() >= 65536
+    assert sink.numel() >= workgroups * 512 and ticks.numel() >= workgroups
+    s = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                        else torch.cuda.current_stream().cuda_stream)
+    f = _fn("tcg_probe_copy_issue", [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp])
+    _check(f(pattern, workgroups, iters, operands.data_ptr(), src.data_ptr(), sink.data_ptr(),
+             ticks.data_ptr(), s), "tcg_probe_copy_issue")
+    return iters * 32 * (COPY_PATTERNS[pattern][1] // 4)

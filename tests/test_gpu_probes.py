@@ -267,3 +267,26 @@ def test_mfma_rate_probe_issues_back_to_back(probe):
     cyc = ticks.cpu().numpy() / (iters * 64)
     print(f"cycles per MFMA: median {np.median(cyc):.2f}", flush=True)
     assert np.all(cyc >= 31.5) and np.median(cyc) <= 40
+
+
+def test_copy_issue_probe_runs_every_pattern(probe):
+    """The copy-issue probe: every pattern runs; without copies the loop
+    issues an MFMA every ~32 cycles per SIMD with one or two waves, and
+    copies never make it faster."""
+    import tensor_core_gemm_amd as tcg
+    wg = 32
+    ops = (torch.randn(8 * 64 * 8) * 0.01).to(torch.bfloat16).view(torch.int16).cuda()
+    src = torch.zeros(65536 // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(wg * 512, device="cuda")
+    ticks = torch.zeros(wg, dtype=torch.int64, device="cuda")
+    got = {}
+    for pat in probe.COPY_PATTERNS:
+        per_simd = probe.copy_issue(pat, wg, 20, ops, src, sink, ticks)
+        torch.cuda.synchronize()
+        got[pat] = float(np.median(ticks.cpu().numpy())) / per_simd
+        assert torch.isfinite(sink[: wg * 256]).all()
+    print(f"cycles per MFMA per SIMD: {got}", flush=True)
+    assert 31.5 <= got[0] <= 40 and 31.5 <= got[3] <= 40
+    assert got[1] >= got[0] * 0.98 and got[4] >= got[3] * 0.98
+    with pytest.raises(RuntimeError):
+        probe.copy_issue(99, wg, 1, ops, src, sink, ticks)
