@@ -139,25 +139,42 @@ def _check(rc: int):
         raise ValueError({-1: "bad argument", -2: "bad dtype", -3: "out of memory"}.get(rc, rc))
 
 
+# What a strided C holds between batch items (16-bit outputs; fp32: its NaN).
+C_SENTINEL16 = 0x7e5a
+C_SENTINEL32 = 0x7fc05a5a
+
+
 def gemm(A, B, M: int, N: int, K: int, in_dtype: int, out_dtype: int, epilogue: int,
          batch: int = 1, stride_a: int | None = None, stride_b: int | None = None,
-         want_y: bool = False, n_threads: int = 0, bias=None):
+         want_y: bool = False, n_threads: int = 0, bias=None, stride_c: int | None = None):
     """C = act(A . B + bias) for [batch][M][K] x [batch][K][N] row-major operands
     (epilogue: the activation code; bias: N fp32 values or None).
 
     Returns C as float32 (out F32) or uint16 patterns (F16/BF16), shape
     [batch, M, N], and, if ``want_y``, the fp32 value before rounding too.
+    With ``stride_c``, C is instead the flat array of (batch - 1) * stride_c
+    + M * N elements that item b fills from b * stride_c, the rest holding
+    C_SENTINEL16 / C_SENTINEL32.
     """
     a, b = _bits(A, in_dtype).reshape(-1), _bits(B, in_dtype).reshape(-1)
     sa = M * K if stride_a is None else stride_a
     sb = K * N if stride_b is None else stride_b
     if batch < 1 or a.size < (batch - 1) * sa + M * K or b.size < (batch - 1) * sb + K * N:
         raise ValueError("operand arrays smaller than the shape and strides need")
-    C = np.zeros((batch, M, N), np.float32 if out_dtype == F32 else np.uint16)
+    if stride_c is not None and stride_c < M * N:
+        raise ValueError("stride_c smaller than one item of C")
+    kind = np.float32 if out_dtype == F32 else np.uint16
+    if stride_c is None:
+        C = np.zeros((batch, M, N), kind)
+        sc = M * N
+    else:
+        sc = stride_c
+        C = np.full((batch - 1) * sc + M * N, C_SENTINEL32 if kind is np.float32 else C_SENTINEL16,
+                    np.uint32 if kind is np.float32 else np.uint16).view(kind)
     Y = np.zeros((batch, M, N), np.float32) if want_y else None
     keep, bp = _bias(bias, N)
     _check(_load().oracle_gemm(M, N, K, in_dtype, out_dtype, epilogue, bp, batch, _ptr(a), sa,
-                               _ptr(b), sb, _ptr(C), M * N, _ptr(Y) if Y is not None else None,
+                               _ptr(b), sb, _ptr(C), sc, _ptr(Y) if Y is not None else None,
                                n_threads))
     return (C, Y) if want_y else C
 

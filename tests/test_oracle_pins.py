@@ -67,7 +67,14 @@ def _encode_inputs(seed=0):
     specials = np.array([0.0, -0.0, np.inf, -np.inf, 65504, 65519.996, 65520, 1e-8, 2**-24,
                          2**-25, 3 * 2**-25], np.float32)
     return np.concatenate([vals, rand_bits, halfway_f16.view(np.float32),
-                           halfway_bf16.view(np.float32), specials]).astype(np.float32)
+                           halfway_bf16.view(np.float32), specials, _nan_inputs()]).astype(np.float32)
+
+
+def _nan_inputs():
+    # the default quiet NaN of both signs, quiet NaNs with low payload bits,
+    # and signalling NaNs (quiet bit clear, payload nonzero)
+    return np.array([0x7fc00000, 0xffc00000, 0x7fc00001, 0x7f800001, 0xff800001, 0x7fa00000,
+                     0x7f802000], np.uint32).view(np.float32)
 
 
 @pytest.mark.parametrize("dtype", [F16, BF16])
@@ -79,6 +86,20 @@ def test_encode_rne_matches_library(dtype):
     assert np.array_equal(got[~nan], ref[~nan])
     # NaN stays NaN (payload not compared)
     assert np.all(np.isnan(values_of(dtype, got[nan])))
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_encode_gives_quiet_nans(dtype):
+    """A NaN, quiet or signalling, converts to a quiet NaN of the narrower
+    format (IEEE 754, conversion of a NaN: the result is a quiet NaN), whatever
+    payload bits survive: exponent all ones, fraction nonzero, and the
+    fraction's top bit set (0x0200 in binary16, 0x0040 in bfloat16)."""
+    got = oracle.encode(dtype, _nan_inputs()).astype(np.uint32)
+    exp_mask, quiet = (0x7c00, 0x0200) if dtype == F16 else (0x7f80, 0x0040)
+    frac_mask = 0x7fff & ~exp_mask
+    assert np.all(got & exp_mask == exp_mask), [hex(v) for v in got]
+    assert np.all(got & frac_mask != 0), [hex(v) for v in got]
+    assert np.all(got & quiet != 0), [hex(v) for v in got]
 
 
 def test_rounding_golden_cases():
@@ -204,8 +225,44 @@ def test_k_zero_gives_positive_zero():
             assert np.all(C.view(np.uint32 if out == F32 else np.uint16) == 0)
 
 
+def test_k_zero_applies_the_epilogue_to_zero():
+    """K = 0 leaves the zero accumulator, and the epilogue still runs on it
+    (page "gizml:tile": Program.zeros, then the epilogue): sigmoid(0) = 1/2,
+    tanh(0) = gelu(0) = 0, and with a bias row, act(bias[j])."""
+    z = np.zeros(0, np.uint16)
+    C = oracle.gemm(z, z, 2, 3, 0, F16, F32, oracle.EPI_SIGMOID)
+    assert np.all(C == 0.5)
+    for epi in (oracle.EPI_TANH, oracle.EPI_GELU, oracle.EPI_GELU_ERF):
+        C = oracle.gemm(z, z, 2, 3, 0, BF16, F32, epi)
+        assert np.all(C.view(np.uint32) == 0)
+    bias = np.array([-1.5, 0.25, 3.0], np.float32)
+    C = oracle.gemm(z, z, 2, 3, 0, F16, F32, EPI_RELU, bias=bias)
+    assert np.array_equal(C[0], np.array([[0.0, 0.25, 3.0]] * 2, np.float32))
+    C = oracle.gemm(z, z, 2, 3, 0, F16, F32, oracle.EPI_SIGMOID, bias=bias)
+    assert np.allclose(C[0, 0], 1.0 / (1.0 + np.exp(-bias.astype(np.float64))), rtol=1e-7, atol=0)
+
+
 # --------------------------------------------------------------------------
 # order and fp32 semantics
+def test_products_round_to_fp32_before_the_sum():
+    """Tile.dot in F32 (page "gizml:tile"): each product is an fp32 value
+    before it joins the sum, so a product beyond fp32's range is infinite even
+    where the partial sum would cancel it, and a product below half of the
+    smallest subnormal is zero.  A fused multiply-add, or a wider accumulator,
+    gives a finite result in the first case and 2^-148 in the second."""
+    # -2^127 * 1 + 2^127 * 2: fl32(2^128) = +Inf, so the sum is +Inf (exact: 2^127)
+    a = np.array([[-(2.0**127), 2.0**127]], np.float32)
+    b = np.array([[1.0], [2.0]], np.float32)
+    C = oracle.gemm(bf16_bits(a), bf16_bits(b), 1, 1, 2, BF16, F32, EPI_NONE)
+    assert np.isposinf(C[0, 0, 0])
+    # 2^-75 * 2^-74 = 2^-149 (the smallest subnormal), then 2^-75 * 2^-75 =
+    # 2^-150 rounds to 0 (a tie, to even), so the sum stays 2^-149
+    a = np.array([[2.0**-75, 2.0**-75]], np.float32)
+    b = np.array([[2.0**-74], [2.0**-75]], np.float32)
+    C = oracle.gemm(bf16_bits(a), bf16_bits(b), 1, 1, 2, BF16, F32, EPI_NONE)
+    assert C.view(np.uint32)[0, 0, 0] == 1
+
+
 def test_fold_runs_k_ascending_in_fp32():
     # bf16 holds 2^24 exactly.  In fp32, k ascending: 2^24 + 1 -> 2^24 (tie to
     # even), + 1 -> 2^24, - 2^24 -> 0.  The exact sum is 2; k descending gives 2.
@@ -290,6 +347,22 @@ def test_relu_of_nan_and_negative_zero():
     assert C[0, 0] == -5.0
 
 
+def test_batch_items_of_c_follow_their_stride():
+    """Item b of C starts at b * stride_c; the elements between items are
+    left as they were."""
+    rng = np.random.default_rng(14)
+    M, N, K, batch, sc = 4, 5, 6, 3, 4 * 5 + 9
+    A = f16_bits(rng.standard_normal(batch * M * K))
+    B = f16_bits(rng.standard_normal(batch * K * N))
+    want = oracle.gemm(A, B, M, N, K, F16, F16, EPI_NONE, batch=batch)
+    flat = oracle.gemm(A, B, M, N, K, F16, F16, EPI_NONE, batch=batch, stride_c=sc)
+    assert flat.shape == ((batch - 1) * sc + M * N,)
+    for b_ in range(batch):
+        assert np.array_equal(flat[b_ * sc:b_ * sc + M * N].reshape(M, N), want[b_])
+        if b_ + 1 < batch:
+            assert np.all(flat[b_ * sc + M * N:(b_ + 1) * sc] == oracle.C_SENTINEL16)
+
+
 def test_batch_items_follow_their_strides():
     rng = np.random.default_rng(12)
     M, N, K, batch = 5, 6, 9, 3
@@ -343,6 +416,12 @@ def test_bad_arguments_are_rejected():
                     bias=np.zeros(3, np.float32))
     with pytest.raises(ValueError):
         oracle.gemm(np.zeros(3, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F16, F32, EPI_NONE)
+    # FP8 is an operand type only: an FP8 output is refused
+    with pytest.raises(ValueError):
+        oracle.gemm(np.zeros(4, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F16, oracle.FP8, EPI_NONE)
+    with pytest.raises(ValueError):
+        oracle.gemm_sampled(np.zeros(4, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F16, oracle.FP8,
+                            EPI_NONE, [0], [0], [0])
 
 
 def test_workload_integer_config_is_exact_by_bound():
