@@ -328,8 +328,16 @@ def main():
 
 
 def make_clock_probe():
+    """The clock probe, its kernel launched once: the first launch of a
+    kernel loads its code (about a millisecond of host time, measured), which
+    inside the timed region would leave the GPU idle and count against every
+    step."""
+    import torch
     from tensor_core_gemm_amd.probe import ClockProbe
-    return ClockProbe()
+    clock = ClockProbe()
+    clock.mark(0)
+    torch.cuda.synchronize()
+    return clock
 
 
 def per_launch_times(step, n, stream):
@@ -382,7 +390,7 @@ def mfma_ceiling(args):
         return probe.mfma_rate(kind, wg, iters, ops, sink, ticks, stream)
 
     flops = step()
-    clock = probe.ClockProbe()
+    clock = make_clock_probe()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
