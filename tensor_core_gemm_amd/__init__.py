@@ -100,8 +100,9 @@ def matmul(A: torch.Tensor, B: torch.Tensor, *, relu: bool = False, act: str | N
     shape = (batch, M, N) if A.dim() == 3 else (M, N)
     if out is None:
         out = torch.empty(shape, dtype=odt, device=A.device)
-    elif tuple(out.shape) != shape or out.dtype != odt or not out.is_contiguous():
-        raise ValueError("out has the wrong shape, dtype or layout")
+    elif tuple(out.shape) != shape or out.dtype != odt or not out.is_contiguous() \
+            or out.device != A.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
     if split_k == 0 and not isinstance(stream, int):
         flags |= FLAG_SPLIT_K
     with torch.cuda.device(A.device):

@@ -205,12 +205,47 @@ def gemm_plan_destroy(plan: Plan) -> None:
     plan.close()
 
 
-def _ptr(x) -> int | None:
+def _ptr(x, need: int = 0, what: str = "buffer") -> int | None:
+    """The device address of a tensor or a raw pointer (an int, passed as
+    is).  A tensor must be a contiguous GPU tensor of at least `need` bytes:
+    a host tensor or a short one would hand the kernels an address they
+    cannot read or write within bounds."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError(f"{what} is not a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} is not contiguous")
+    have = x.numel() * x.element_size()
+    if have < need:
+        raise ValueError(f"{what} holds {have} bytes; the plan needs {need}")
     return x.data_ptr()
+
+
+_IN_BYTES = {F16: 2, BF16: 2, FP8: 1}
+_OUT_BYTES = {F32: 4, F16: 2, BF16: 2}
+
+
+def _extent(batch: int, stride: int, rows: int, cols: int) -> int:
+    """Elements an operand spans: one item, or batch items `stride` apart."""
+    if rows == 0 or cols == 0:
+        return 0
+    return rows * cols if batch <= 1 else (batch - 1) * stride + rows * cols
+
+
+def _operands(desc: gemm_desc, A, B, C, bias=None):
+    """Device addresses of A, B, C (and bias), tensors checked against the
+    sizes the description implies."""
+    if desc is None:  # no description to size against (the library rejects such a plan)
+        return _ptr(A, 0, "A"), _ptr(B, 0, "B"), _ptr(C, 0, "C"), _ptr(bias, 0, "bias")
+    ib, ob = _IN_BYTES.get(desc.in_dtype, 2), _OUT_BYTES.get(desc.out_dtype, 4)
+    b = desc.batch
+    return (_ptr(A, _extent(b, desc.stride_a, desc.M, desc.K) * ib, "A"),
+            _ptr(B, _extent(b, desc.stride_b, desc.K, desc.N) * ib, "B"),
+            _ptr(C, _extent(b, desc.stride_c, desc.M, desc.N) * ob, "C"),
+            _ptr(bias, desc.N * 4 if bias is not None else 0, "bias"))
 
 
 def _stream(stream) -> int:
@@ -225,7 +260,8 @@ def gemm_run(plan: Plan, A, B, C, stream=None) -> None:
     """Launch on `stream` (a torch.cuda.Stream, a raw hipStream_t int, or
     None for torch's current stream).  A, B, C are device tensors or raw
     device pointers; nothing is synchronised."""
-    _check(_fn("gemm_run")(plan.handle, _ptr(A), _ptr(B), _ptr(C), _stream(stream)), "gemm_run")
+    a, b, c, _ = _operands(plan.desc, A, B, C)
+    _check(_fn("gemm_run")(plan.handle, a, b, c, _stream(stream)), "gemm_run")
 
 
 def gemm_run_ex(plan: Plan, A, B, C, bias=None, workspace=None, workspace_bytes=None,
@@ -237,16 +273,17 @@ def gemm_run_ex(plan: Plan, A, B, C, bias=None, workspace=None, workspace_bytes=
         workspace_bytes = 0
         if workspace is not None and not isinstance(workspace, int):
             workspace_bytes = workspace.numel() * workspace.element_size()
-    args = gemm_run_args(_ptr(bias), _ptr(workspace), workspace_bytes)
-    _check(_fn("gemm_run_ex")(plan.handle, _ptr(A), _ptr(B), _ptr(C), ctypes.byref(args),
-                              _stream(stream)), "gemm_run_ex")
+    a, b, c, bp = _operands(plan.desc, A, B, C, bias)
+    args = gemm_run_args(bp, _ptr(workspace, 0, "workspace"), workspace_bytes)
+    _check(_fn("gemm_run_ex")(plan.handle, a, b, c, ctypes.byref(args), _stream(stream)),
+           "gemm_run_ex")
 
 
 def gemm_run_noalloc(plan: Plan, A, B, C, bias=None, stream=None) -> None:
     """gemm_run_ex with the library's fixed device array as the split-K
     workspace (no device allocation; calls that overlap on one GPU race)."""
-    _check(_fn("gemm_run_noalloc")(plan.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias),
-                                   _stream(stream)), "gemm_run_noalloc")
+    a, b, c, bp = _operands(plan.desc, A, B, C, bias)
+    _check(_fn("gemm_run_noalloc")(plan.handle, a, b, c, bp, _stream(stream)), "gemm_run_noalloc")
 
 
 def check_runtime() -> None:
@@ -270,9 +307,10 @@ def gemm_autotune(desc: gemm_desc, A, B, C, bias=None, workspace=None, workspace
         workspace_bytes = 0
         if workspace is not None and not isinstance(workspace, int):
             workspace_bytes = workspace.numel() * workspace.element_size()
-    args = gemm_run_args(_ptr(bias), _ptr(workspace), workspace_bytes)
+    a, b, c, bp = _operands(desc, A, B, C, bias)
+    args = gemm_run_args(bp, _ptr(workspace, 0, "workspace"), workspace_bytes)
     h = _vp()
-    _check(_fn("gemm_autotune")(ctypes.byref(desc), _ptr(A), _ptr(B), _ptr(C), ctypes.byref(args),
+    _check(_fn("gemm_autotune")(ctypes.byref(desc), a, b, c, ctypes.byref(args),
                                 _stream(stream), ctypes.byref(h)), "gemm_autotune")
     return Plan(h.value, desc)
 

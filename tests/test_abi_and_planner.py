@@ -418,3 +418,23 @@ def test_tuned_split_tail_entry_replays_the_planners_tail_plan(tmp_path):
     tcg.gemm_tune_cache_save(str(g))
     assert g.read_text().split()[13:15] == [str(ref.tile_id), "0"]
     tcg.gemm_tune_cache_clear()
+
+
+def test_run_refuses_host_tensors_before_any_launch():
+    """The binding hands the kernels device addresses only: a host tensor is
+    refused in Python, before the library is called (a host address would
+    be written through by the GPU)."""
+    import torch
+    plan = tcg.gemm_plan_for_caps(tcg.make_desc(64, 64, 64, BF16, BF16, EPI_NONE), tcg.make_caps())
+    A = torch.zeros(64, 64, dtype=torch.bfloat16)
+    for fn in (tcg.gemm_run, tcg.gemm_run_ex, tcg.gemm_run_noalloc):
+        with pytest.raises(ValueError, match="not a GPU tensor"):
+            fn(plan, A, A, A, stream=0)
+
+
+def test_operand_extents_follow_the_batch_strides():
+    from tensor_core_gemm_amd.capi import _extent
+    assert _extent(1, 0, 5, 7) == 35
+    assert _extent(1, 999, 5, 7) == 35          # one item: the stride is not used
+    assert _extent(3, 40, 5, 7) == 2 * 40 + 35  # the last item ends M*K past its start
+    assert _extent(3, 40, 0, 7) == 0
