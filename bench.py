@@ -284,7 +284,8 @@ def main():
         pass
 
     result = {
-        "metric": METRIC,
+        # the headline's metric; another workload's line names that workload
+        "metric": METRIC if w.name == "bf16_4096_relu" else f"GEMM TFLOP/s ({w.name})",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
