@@ -307,19 +307,22 @@ int gemm_run_noalloc(gemm_plan_t plan, const void* A, const void* B, void* C, co
  * exact, and the run may not read what it writes).
  *
  * Candidates are every tile configuration (desc->tile == 0) or the one
- * given, each unsplit and, with GEMM_FLAG_SPLIT_K, split into 2, 4, 8 or 16
- * ranges of at least 4 trips where args->workspace holds the partial sums;
- * with GEMM_FLAG_SPLIT_K and desc->tile == 0 also the planner's own plan
- * where it splits K for the bottom rows only (gemm_plan_info.tail_rows > 0)
- * and the workspace holds its partial sums.
+ * given; each unsplit and, with GEMM_FLAG_SPLIT_K, split into 2, 4, 8 or 16
+ * ranges of at least 4 trips where args->workspace holds the partial sums,
+ * or (desc->split_k > 0) split into exactly desc->split_k ranges; with
+ * GEMM_FLAG_SPLIT_K, desc->tile == 0 and desc->split_k == 0 also the
+ * planner's own plan where it splits K for the bottom rows only
+ * (gemm_plan_info.tail_rows > 0) and the workspace holds its partial sums.
  * Each candidate runs once to warm up, then 5 times, each timed with HIP
  * events on `stream`; the smallest time wins.  A and B are read; C and the
  * workspace are written many times; the bias (GEMM_FLAG_BIAS) is read.
  * The call synchronises `stream` and returns a new plan for the winner in
- * *out (the caller destroys it).  The choice is kept in a process-wide
- * cache keyed by the device's architecture and CU count and by every field
- * of desc but tile, split_k and GEMM_FLAG_TUNED; gemm_plan with
- * GEMM_FLAG_TUNED reads it.  Errors: as gemm_plan and gemm_run_ex, and
+ * *out (the caller destroys it).  The choice of an unrestricted search
+ * (desc->tile == 0, desc->split_k == 0) is kept in a process-wide cache
+ * keyed by the device's architecture and CU count and by every field of
+ * desc but tile, split_k and GEMM_FLAG_TUNED; gemm_plan with
+ * GEMM_FLAG_TUNED reads it.  A search restricted to a tile or a split
+ * returns its winner without caching it.  Errors: as gemm_plan and gemm_run_ex, and
  * GEMM_E_LAUNCH if timing fails.
  */
 int gemm_autotune(const gemm_desc* desc, const void* A, const void* B, void* C, const gemm_run_args* args,

@@ -861,11 +861,15 @@ extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B
     *err = r;
     return t_min;
   };
+  // A description that names a tile or a split restricts the search to it;
+  // such a result answers only that question and is not cached.
+  const bool restricted = base.tile != 0 || base.split_k != 0;
   for (int id = lo; id <= hi && rc == GEMM_OK; ++id) {
     if (tcg::kTiles[id - 1].esize != in_size(base.in_dtype)) continue;  // built for the other width
     int last_split = 0;
-    for (int sp = 1; sp <= 16; sp *= 2) {
-      if (sp > 1 && !(base.flags & GEMM_FLAG_SPLIT_K)) break;
+    const int sp_first = base.split_k > 0 ? base.split_k : 1;
+    const int sp_last = base.split_k > 0 ? base.split_k : ((base.flags & GEMM_FLAG_SPLIT_K) ? 16 : 1);
+    for (int sp = sp_first; sp <= sp_last; sp *= 2) {
       gemm_desc d = base;
       d.tile = id;
       d.split_k = sp;
@@ -874,7 +878,7 @@ extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B
       if (gemm_plan_for_caps(&d, &caps, &h) != GEMM_OK) continue;
       const gemm_plan_info& in = reinterpret_cast<Plan*>(h)->info;
       const bool usable = in.split_k == sp && in.split_k != last_split && in.workspace_bytes <= ws_have &&
-                          (sp == 1 || in.trips_per_split >= 4);
+                          (sp == 1 || base.split_k > 0 || in.trips_per_split >= 4);
       if (!usable) {
         gemm_plan_destroy(h);
         continue;
@@ -918,7 +922,7 @@ extern "C" int gemm_autotune(const gemm_desc* desc, const void* A, const void* B
   (void)hipGetLastError();
   if (rc != GEMM_OK) return rc;
   if (best.tile == 0) return GEMM_E_PLAN;  // no candidate could run
-  {
+  if (!restricted) {
     std::lock_guard<std::mutex> lk(g_tune_mu);
     g_tune[tune_key(base, caps)] = best;
   }

@@ -131,3 +131,30 @@ def test_autotune_considers_the_planners_split_tail(tcg):
     want, _ = oracle.gemm_sampled(A, B, M, N, K, BF16, F32, EPI_RELU, bi, ii, jj)
     assert np.array_equal(C.cpu().numpy()[ii, jj], want)
     tcg.gemm_tune_cache_clear()
+
+
+def test_a_restricted_search_answers_without_caching(tcg):
+    """A description naming a tile or a split restricts the candidates to it,
+    and its winner is returned but not cached (a later GEMM_FLAG_TUNED plan
+    must not replay a partial search)."""
+    tcg.gemm_tune_cache_clear()
+    M, N, K = 256, 512, 8192
+    w = gw.custom(M, N, K, BF16, F32, EPI_NONE, gw.INT4, seed=93)
+    A, B = gw.make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(16 * M * N, dtype=torch.float32, device="cuda")
+    note("autotune restricted to tile 2")
+    p = tcg.gemm_autotune(tcg.make_desc(M, N, K, BF16, F32, EPI_NONE, tcg.FLAG_SPLIT_K, tile=2),
+                          Ad, Bd, C, workspace=ws)
+    assert p.info().tile_id == 2
+    assert tcg.gemm_tune_cache_size() == 0
+    note("autotune restricted to 3 ranges")
+    p3 = tcg.gemm_autotune(tcg.make_desc(M, N, K, BF16, F32, EPI_NONE, 0, split_k=3),
+                           Ad, Bd, C, workspace=ws)
+    assert p3.info().split_k == 3
+    assert tcg.gemm_tune_cache_size() == 0
+    C.fill_(float("nan"))
+    tcg.gemm_run_ex(p3, Ad, Bd, C, workspace=ws)
+    torch.cuda.synchronize()
+    check_against_oracle(w, A, B, C.cpu().reshape(1, M, N))
