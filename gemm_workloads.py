@@ -114,13 +114,15 @@ WORKLOADS = {
 
 
 def draw(shape, dist: Dist, dtype: int, gen: torch.Generator) -> torch.Tensor:
-    """fp32 draw on the CPU, then rounded to the 16-bit storage type."""
+    """fp32 draw on the generator's device (the CPU for the workloads), then
+    rounded to the 16-bit storage type."""
+    dev = gen.device
     if dist.kind == "normal":
-        x = torch.randn(shape, generator=gen, dtype=torch.float32) * dist.b + dist.a
+        x = torch.randn(shape, generator=gen, dtype=torch.float32, device=dev) * dist.b + dist.a
     elif dist.kind == "randint":
-        x = torch.randint(int(dist.a), int(dist.b) + 1, shape, generator=gen).to(torch.float32)
+        x = torch.randint(int(dist.a), int(dist.b) + 1, shape, generator=gen, device=dev).to(torch.float32)
     elif dist.kind == "uniform":
-        x = torch.rand(shape, generator=gen, dtype=torch.float32) * (dist.b - dist.a) + dist.a
+        x = torch.rand(shape, generator=gen, dtype=torch.float32, device=dev) * (dist.b - dist.a) + dist.a
     else:
         raise ValueError(dist.kind)
     return x.to(TORCH_DTYPE[dtype])

@@ -438,3 +438,17 @@ def test_operand_extents_follow_the_batch_strides():
     assert _extent(1, 999, 5, 7) == 35          # one item: the stride is not used
     assert _extent(3, 40, 5, 7) == 2 * 40 + 35  # the last item ends M*K past its start
     assert _extent(3, 40, 0, 7) == 0
+
+
+def test_the_256_row_tile_takes_k_up_to_its_31_bit_row_offsets():
+    """The 256 x 256 tile addresses row r of its A block at byte offset
+    r * K * 2 inside a buffer resource of at most 2^31 - 1 bytes: K up to
+    4194303 plans on it (16-byte copies up to 4194296), 4194304 is refused."""
+    caps = tcg.make_caps()
+    ok = tcg.gemm_plan_for_caps(tcg.make_desc(256, 64, 4194296, BF16, BF16, EPI_NONE, tile=1), caps)
+    assert (ok.info().tile_id, ok.info().vec16) == (1, 1)
+    ok = tcg.gemm_plan_for_caps(tcg.make_desc(256, 64, 4194303, BF16, BF16, EPI_NONE, tile=1), caps)
+    assert (ok.info().tile_id, ok.info().vec16) == (1, 0)
+    with pytest.raises(tcg.GemmError) as e:
+        tcg.gemm_plan_for_caps(tcg.make_desc(256, 64, 4194304, BF16, BF16, EPI_NONE, tile=1), caps)
+    assert e.value.code == tcg.GEMM_E_SIZE
