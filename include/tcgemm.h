@@ -369,7 +369,7 @@ int gemm_stage_depth(const gemm_device_caps* caps, int64_t used, const int64_t* 
 int gemm_tile_count(void);
 
 /* HIP runtime version the library is running against (hipRuntimeGetVersion),
- * or -1.  A diagnostic of this build with no counterpart on the pages: a
+ * or -1.  A diagnostic of the library with no counterpart on the pages: a
  * process must run the library on the runtime its caller's device pointers
  * and streams come from. */
 int gemm_runtime_version(void);
