@@ -235,17 +235,31 @@ def _extent(batch: int, stride: int, rows: int, cols: int) -> int:
     return rows * cols if batch <= 1 else (batch - 1) * stride + rows * cols
 
 
-def _operands(desc: gemm_desc, A, B, C, bias=None):
-    """Device addresses of A, B, C (and bias), tensors checked against the
-    sizes the description implies."""
-    if desc is None:  # no description to size against (the library rejects such a plan)
-        return _ptr(A, 0, "A"), _ptr(B, 0, "B"), _ptr(C, 0, "C"), _ptr(bias, 0, "bias")
+def _needs(desc: gemm_desc | None) -> tuple:
+    """Bytes A, B, C and a bias must hold for a description (none without one:
+    the library rejects a plan that has none)."""
+    if desc is None:
+        return 0, 0, 0, 0
     ib, ob = _IN_BYTES.get(desc.in_dtype, 2), _OUT_BYTES.get(desc.out_dtype, 4)
     b = desc.batch
-    return (_ptr(A, _extent(b, desc.stride_a, desc.M, desc.K) * ib, "A"),
-            _ptr(B, _extent(b, desc.stride_b, desc.K, desc.N) * ib, "B"),
-            _ptr(C, _extent(b, desc.stride_c, desc.M, desc.N) * ob, "C"),
-            _ptr(bias, desc.N * 4 if bias is not None else 0, "bias"))
+    return (_extent(b, desc.stride_a, desc.M, desc.K) * ib, _extent(b, desc.stride_b, desc.K, desc.N) * ib,
+            _extent(b, desc.stride_c, desc.M, desc.N) * ob, desc.N * 4)
+
+
+def _operands(needs: tuple, A, B, C, bias=None):
+    """Device addresses of A, B, C (and bias), tensors checked against the
+    byte counts of `needs`."""
+    return (_ptr(A, needs[0], "A"), _ptr(B, needs[1], "B"), _ptr(C, needs[2], "C"),
+            _ptr(bias, needs[3], "bias"))
+
+
+def _plan_needs(plan) -> tuple:
+    """_needs of a plan's description, computed once (a plan is immutable)."""
+    n = plan.__dict__.get("_needs")
+    if n is None:
+        n = _needs(plan.desc)
+        plan._needs = n
+    return n
 
 
 def _stream(stream) -> int:
@@ -260,7 +274,7 @@ def gemm_run(plan: Plan, A, B, C, stream=None) -> None:
     """Launch on `stream` (a torch.cuda.Stream, a raw hipStream_t int, or
     None for torch's current stream).  A, B, C are device tensors or raw
     device pointers; nothing is synchronised."""
-    a, b, c, _ = _operands(plan.desc, A, B, C)
+    a, b, c, _ = _operands(_plan_needs(plan), A, B, C)
     _check(_fn("gemm_run")(plan.handle, a, b, c, _stream(stream)), "gemm_run")
 
 
@@ -273,7 +287,7 @@ def gemm_run_ex(plan: Plan, A, B, C, bias=None, workspace=None, workspace_bytes=
         workspace_bytes = 0
         if workspace is not None and not isinstance(workspace, int):
             workspace_bytes = workspace.numel() * workspace.element_size()
-    a, b, c, bp = _operands(plan.desc, A, B, C, bias)
+    a, b, c, bp = _operands(_plan_needs(plan), A, B, C, bias)
     args = gemm_run_args(bp, _ptr(workspace, 0, "workspace"), workspace_bytes)
     _check(_fn("gemm_run_ex")(plan.handle, a, b, c, ctypes.byref(args), _stream(stream)),
            "gemm_run_ex")
@@ -282,7 +296,7 @@ def gemm_run_ex(plan: Plan, A, B, C, bias=None, workspace=None, workspace_bytes=
 def gemm_run_noalloc(plan: Plan, A, B, C, bias=None, stream=None) -> None:
     """gemm_run_ex with the library's fixed device array as the split-K
     workspace (no device allocation; calls that overlap on one GPU race)."""
-    a, b, c, bp = _operands(plan.desc, A, B, C, bias)
+    a, b, c, bp = _operands(_plan_needs(plan), A, B, C, bias)
     _check(_fn("gemm_run_noalloc")(plan.handle, a, b, c, bp, _stream(stream)), "gemm_run_noalloc")
 
 
@@ -307,7 +321,7 @@ def gemm_autotune(desc: gemm_desc, A, B, C, bias=None, workspace=None, workspace
         workspace_bytes = 0
         if workspace is not None and not isinstance(workspace, int):
             workspace_bytes = workspace.numel() * workspace.element_size()
-    a, b, c, bp = _operands(desc, A, B, C, bias)
+    a, b, c, bp = _operands(_needs(desc), A, B, C, bias)
     args = gemm_run_args(bp, _ptr(workspace, 0, "workspace"), workspace_bytes)
     h = _vp()
     _check(_fn("gemm_autotune")(ctypes.byref(desc), a, b, c, ctypes.byref(args),
