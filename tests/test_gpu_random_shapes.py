@@ -73,3 +73,53 @@ def test_random_problem_matches_the_oracle(tcg, case):
     if tile:
         assert p.info().tile_id == tile
     check_against_oracle(w, A, B, C, bias=b)
+
+
+GUARD = 64
+SENTINEL = 0x5A5A
+
+
+def wide_cases(n=40, seed=20261203):
+    """Batches of up to 3 items, sides up to 1200 (many ragged trips on every
+    tile), the stage and split flags, operands shifted off 16-byte alignment
+    (the element-copy path), and guard bands around C."""
+    rng = random.Random(seed)
+    flag_names = ["none", "stages1", "unstaged", "stages2", "split"]
+    out = []
+    for i in range(n):
+        in_dtype = rng.choice([F16, BF16, FP8])
+        out_dtype = rng.choice([F32, F16, BF16])
+        batch = rng.choice([1, 1, 2, 3])
+        M = rng.randint(1, 1200)
+        N = rng.choice([rng.randint(1, 1200), rng.choice([8, 256, 520, 1024])])
+        K = rng.choice([rng.randint(1, 1200), rng.choice([0, 64, 128, 1000, 1024])])
+        epi = rng.choice([0, 1, 1, 2, 3, 4, 5])
+        bias = rng.random() < 0.3
+        dist = gw.INT4 if (rng.random() < 0.4 and epi in (0, 1) and not bias) else gw.NORMAL
+        flag = rng.choice(flag_names)
+        shift = rng.choice([0, 0, 0, 1, 3])
+        tile = 0 if rng.random() < 0.5 else rng.choice(FP8_TILES if in_dtype == FP8 else
+                                                         [t for t in SIXTEEN_BIT_TILES])
+        out.append((i, batch, M, N, K, in_dtype, out_dtype, epi, bias, dist, flag, shift, tile))
+    return out
+
+
+@pytest.mark.parametrize("case", wide_cases(), ids=lambda c: f"wide{c[0]}")
+def test_wide_random_problem_matches_the_oracle(tcg, case):
+    i, batch, M, N, K, in_dtype, out_dtype, epi, bias, dist, flag, shift, tile = case
+    w = gw.custom(M, N, K, in_dtype, out_dtype, epi, dist, seed=3000 + i, batch=batch)
+    A, B = gw.make_inputs(w)
+    b = gw.draw_bias(N, gw.NORMAL, seed=4000 + i) if bias else None
+    flags = {"none": 0, "stages1": tcg.FLAG_FORCE_STAGES_1, "unstaged": tcg.FLAG_UNSTAGED,
+             "stages2": tcg.FLAG_FORCE_STAGES_2, "split": tcg.FLAG_SPLIT_K}[flag]
+    if K == 0:
+        A = torch.zeros(0, dtype=A.dtype)
+        B = torch.zeros(0, dtype=B.dtype)
+    sentinel = SENTINEL | (SENTINEL << 16) if out_dtype == F32 else SENTINEL
+    C, buf, p = run(tcg, A, B, w, flags=flags, tile=tile, bias=b, a_offset=shift, b_offset=shift,
+                    guard=GUARD, sentinel=sentinel)
+    if tile:
+        assert p.info().tile_id == tile
+    bits = buf.view(torch.int32 if out_dtype == F32 else torch.int16)
+    assert torch.all(bits[:GUARD] == sentinel) and torch.all(bits[-GUARD:] == sentinel), "guard band written"
+    check_against_oracle(w, A, B, C, bias=b)
