@@ -75,14 +75,14 @@ def test_random_problem_matches_the_oracle(tcg, case):
     check_against_oracle(w, A, B, C, bias=b)
 
 
-GUARD = 64
 SENTINEL = 0x5A5A
 
 
-def wide_cases(n=40, seed=20261203):
+def wide_cases(n=60, seed=20261203):
     """Batches of up to 3 items, sides up to 1200 (many ragged trips on every
     tile), the stage and split flags, operands shifted off 16-byte alignment
-    (the element-copy path), and guard bands around C."""
+    (the element-copy path), and guard bands around C whose length also
+    shifts C (a guard of 1 or 63 elements: the element-by-element stores)."""
     rng = random.Random(seed)
     flag_names = ["none", "stages1", "unstaged", "stages2", "split"]
     out = []
@@ -100,13 +100,14 @@ def wide_cases(n=40, seed=20261203):
         shift = rng.choice([0, 0, 0, 1, 3])
         tile = 0 if rng.random() < 0.5 else rng.choice(FP8_TILES if in_dtype == FP8 else
                                                          [t for t in SIXTEEN_BIT_TILES])
-        out.append((i, batch, M, N, K, in_dtype, out_dtype, epi, bias, dist, flag, shift, tile))
+        guard = rng.choice([64, 64, 63, 1])
+        out.append((i, batch, M, N, K, in_dtype, out_dtype, epi, bias, dist, flag, shift, tile, guard))
     return out
 
 
 @pytest.mark.parametrize("case", wide_cases(), ids=lambda c: f"wide{c[0]}")
 def test_wide_random_problem_matches_the_oracle(tcg, case):
-    i, batch, M, N, K, in_dtype, out_dtype, epi, bias, dist, flag, shift, tile = case
+    i, batch, M, N, K, in_dtype, out_dtype, epi, bias, dist, flag, shift, tile, guard = case
     w = gw.custom(M, N, K, in_dtype, out_dtype, epi, dist, seed=3000 + i, batch=batch)
     A, B = gw.make_inputs(w)
     b = gw.draw_bias(N, gw.NORMAL, seed=4000 + i) if bias else None
@@ -117,9 +118,9 @@ def test_wide_random_problem_matches_the_oracle(tcg, case):
         B = torch.zeros(0, dtype=B.dtype)
     sentinel = SENTINEL | (SENTINEL << 16) if out_dtype == F32 else SENTINEL
     C, buf, p = run(tcg, A, B, w, flags=flags, tile=tile, bias=b, a_offset=shift, b_offset=shift,
-                    guard=GUARD, sentinel=sentinel)
+                    guard=guard, sentinel=sentinel)
     if tile:
         assert p.info().tile_id == tile
     bits = buf.view(torch.int32 if out_dtype == F32 else torch.int16)
-    assert torch.all(bits[:GUARD] == sentinel) and torch.all(bits[-GUARD:] == sentinel), "guard band written"
+    assert torch.all(bits[:guard] == sentinel) and torch.all(bits[-guard:] == sentinel), "guard band written"
     check_against_oracle(w, A, B, C, bias=b)
