@@ -124,3 +124,40 @@ def test_wide_random_problem_matches_the_oracle(tcg, case):
     bits = buf.view(torch.int32 if out_dtype == F32 else torch.int16)
     assert torch.all(bits[:guard] == sentinel) and torch.all(bits[-guard:] == sentinel), "guard band written"
     check_against_oracle(w, A, B, C, bias=b)
+
+
+def split_cases(n=40, seed=20261204):
+    """Explicit K splits of 2 to 16 ranges (the reduction applies the bias,
+    the activation and the output rounding), on any tile, batches of up to
+    2 items."""
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        in_dtype = rng.choice([F16, BF16, FP8])
+        out_dtype = rng.choice([F32, F16, BF16])
+        split = rng.choice([2, 3, 4, 5, 8, 16])
+        M = rng.randint(1, 600)
+        N = rng.randint(1, 600)
+        K = rng.randint(64 * split, 3000)
+        epi = rng.choice([0, 1, 2, 3, 4, 5])
+        bias = rng.random() < 0.5
+        dist = gw.INT4 if (rng.random() < 0.4 and epi in (0, 1) and not bias) else gw.NORMAL
+        batch = rng.choice([1, 1, 2])
+        tile = 0 if rng.random() < 0.4 else rng.choice(FP8_TILES if in_dtype == FP8 else SIXTEEN_BIT_TILES)
+        out.append((i, batch, M, N, K, in_dtype, out_dtype, epi, bias, dist, split, tile))
+    return out
+
+
+@pytest.mark.parametrize("case", split_cases(), ids=lambda c: f"split{c[0]}")
+def test_split_random_problem_matches_the_oracle(tcg, case):
+    i, batch, M, N, K, in_dtype, out_dtype, epi, bias, dist, split, tile = case
+    w = gw.custom(M, N, K, in_dtype, out_dtype, epi, dist, seed=5000 + i, batch=batch)
+    A, B = gw.make_inputs(w)
+    b = gw.draw_bias(N, gw.NORMAL, seed=6000 + i) if bias else None
+    C, _, p = run(tcg, A, B, w, tile=tile, bias=b, split_k=split)
+    info = p.info()
+    if tile:
+        assert info.tile_id == tile
+    # the planner keeps ranges of whole trips: at most `split` of them
+    assert 1 <= info.split_k <= split
+    check_against_oracle(w, A, B, C, bias=b)
