@@ -452,3 +452,24 @@ def test_the_256_row_tile_takes_k_up_to_its_31_bit_row_offsets():
     with pytest.raises(tcg.GemmError) as e:
         tcg.gemm_plan_for_caps(tcg.make_desc(256, 64, 4194304, BF16, BF16, EPI_NONE, tile=1), caps)
     assert e.value.code == tcg.GEMM_E_SIZE
+
+
+def test_outputs_filling_one_round_of_256x128_take_that_tile():
+    """16-bit operands, one batch item, K up to 4096, M a multiple of 256 and
+    N of 128, the 256 x 128 grid filling between 3/4 of the CUs and all of
+    them: the 256 x 128 tile (measured faster than the 128 x 128 one)."""
+    for M, N, K in ((8192, 1024, 1024), (4096, 2048, 2048), (2048, 4096, 4096), (1024, 8192, 1024),
+                    (7168, 1024, 512)):
+        for flags in (0, tcg.FLAG_SPLIT_K):
+            i = plan(M, N, K, flags=flags).info()
+            assert (i.tile_id, i.workgroups, i.split_k) == (12, (M // 256) * (N // 128), 1), (M, N, K)
+    # not where the grid is smaller, larger or ragged, K longer, FP8, or batched
+    assert plan(2304, 2304, 2304).info().tile_id != 12       # 162 tiles: under 3/4 of the CUs
+    assert plan(4608, 4608, 4608).info().tile_id != 12       # 648 tiles
+    assert plan(8192, 1000, 1024).info().tile_id != 12       # ragged N
+    assert plan(8192, 1024, 8192).info().tile_id != 12       # long K: left to the time model
+    assert plan(8192, 1024, 1024, in_dtype=tcg.FP8).info().tile_id != 12
+    assert plan(8192, 1024, 1024, batch=2, sa=8192 * 1024, sb=1024 * 1024,
+                sc=8192 * 1024).info().tile_id != 12
+    # a device with fewer CUs changes what one round is
+    assert plan(4096, 1024, 1024, caps=tcg.make_caps(num_cus=128)).info().tile_id == 12
