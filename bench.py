@@ -24,10 +24,15 @@ duration from a separate pass with an event after every launch.
 cpu_baseline: the CPU oracle (plain C, fp32, OpenMP) timed on this host's
 cores on a bounded sample of the same workload: the first r rows of C
 (r x N x K multiply-adds), r chosen so the oracle works about 12 s; then on
-one thread (about 6 s); with the CPU model.
+one thread (about 6 s); with the CPU model.  This leg is the only part of
+the script that runs the oracle; it also checks 64 outputs of the last
+timed step against it (timed_output_check).
 
 --mfma-ceiling: the register-only MFMA loop instead of the GEMM (the MFMA
-units' sustained rate on N(0, 1) bf16 operands and the clock they run at).
+units' sustained rate on N(0, 1) bf16 or FP8 operands and the clock they run
+at); --copy-issue-cost: MFMA loops with global->LDS copies in between;
+--planner-sweep: the planner's plan, the autotuner's and torch.matmul on a
+sweep of shapes.
 """
 from __future__ import annotations
 
