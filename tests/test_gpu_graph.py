@@ -27,22 +27,28 @@ def tcg():
 
 
 CASES = [
-    # (workload, plan flags, tile): a single-kernel plan, a split plan (GEMM
-    # plus reduction), and the persistent short-K tile
-    (gw.custom(1000, 1000, 1000, F16, F16, EPI_RELU, gw.NORMAL, seed=41), 0, 0, 0),
-    (gw.custom(512, 512, 8192, BF16, BF16, EPI_NONE, gw.NORMAL, seed=42), 0, 0, 4),
-    (gw.custom(40000, 288, 96, F16, F16, EPI_NONE, gw.NORMAL, seed=43), 0, 11, 0),
+    # (workload, planner may split, tile, split): a single-kernel plan, a
+    # split plan (GEMM plus reduction), the persistent short-K tile, and the
+    # planner's split tail (the unsplit rows, then the last round's rows
+    # split in K, then their reduction: three launches)
+    (gw.custom(1000, 1000, 1000, F16, F16, EPI_RELU, gw.NORMAL, seed=41), False, 0, 0),
+    (gw.custom(512, 512, 8192, BF16, BF16, EPI_NONE, gw.NORMAL, seed=42), False, 0, 4),
+    (gw.custom(40000, 288, 96, F16, F16, EPI_NONE, gw.NORMAL, seed=43), False, 11, 0),
+    (gw.custom(4352, 4352, 2048, BF16, BF16, EPI_RELU, gw.NORMAL, seed=44), True, 0, 0),
 ]
 
 
-@pytest.mark.parametrize("w,flags,tile,split", CASES, ids=["single", "split", "short_k"])
-def test_captured_runs_replay_the_eager_result(tcg, w, flags, tile, split):
+@pytest.mark.parametrize("w,may_split,tile,split", CASES, ids=["single", "split", "short_k", "split_tail"])
+def test_captured_runs_replay_the_eager_result(tcg, w, may_split, tile, split):
     A, B = gw.make_inputs(w)
     Ad, Bd = A.cuda(), B.cuda()
     odt = gw.TORCH_DTYPE[w.out_dtype]
+    flags = tcg.FLAG_SPLIT_K if may_split else 0
     p = tcg.gemm_plan(tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue, flags,
                                     tile=tile, split_k=split))
     note(f"graph capture {w.name}: {p.describe()}")
+    if may_split:
+        assert p.info().tail_rows > 0  # the case is the split tail
     ws_bytes = p.info().workspace_bytes
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()

@@ -79,6 +79,50 @@ def test_noalloc_full_size_split_plan_and_epilogues():
     check_against_oracle(wn, A, B, C_na.reshape(1, wn.M, wn.N))
 
 
+@pytest.mark.gpu
+def test_noalloc_under_graph_capture_replays_the_eager_result():
+    """The callers this entry point is for include code under HIP graph
+    capture.  A split-tail plan (three launches, the partial sums in the
+    fixed array) is called once eagerly, then captured; between replays an
+    eager call of another split plan overwrites the array, and every replay
+    must still give the eager result bit for bit."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = gw.custom(4352, 4352, 2048, BF16, BF16, EPI_RELU, gw.NORMAL, seed=76, name="na_graph")
+    A, B = gw.make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    p = tcg.gemm_plan(tcg.make_desc(w.M, w.N, w.K, w.in_dtype, w.out_dtype, w.epilogue,
+                                    tcg.FLAG_SPLIT_K))
+    info = p.info()
+    note(f"noalloc graph {w.name}: {p.describe()}")
+    assert info.tail_rows > 0 and 0 < info.workspace_bytes <= tcg.NOALLOC_SCRATCH_BYTES
+    wo = gw.custom(512, 1024, 4096, BF16, BF16, EPI_NONE, gw.NORMAL, seed=77, name="na_other")
+    Ao, Bo = (t.cuda() for t in gw.make_inputs(wo))
+    po = tcg.gemm_plan(tcg.make_desc(wo.M, wo.N, wo.K, wo.in_dtype, wo.out_dtype, wo.epilogue, 0,
+                                     tile=1, split_k=4))
+    Co = torch.empty((wo.M, wo.N), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+
+    C_eager = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(s):
+        tcg.gemm_run_noalloc(p, Ad, Bd, C_eager, stream=s)
+    torch.cuda.synchronize()
+    eager = as_bits(C_eager.cpu())
+    check_against_oracle(w, A, B, C_eager.cpu().reshape(1, w.M, w.N))
+
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        tcg.gemm_run_noalloc(p, Ad, Bd, C, stream=s)
+    for r in range(4):
+        C.fill_(float("nan"))
+        tcg.gemm_run_noalloc(po, Ao, Bo, Co)    # eager work that overwrites the array
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(as_bits(C.cpu()), eager), f"replay {r}"
+
+
 def test_noalloc_refuses_a_workspace_beyond_the_array():
     """A plan whose partial sums exceed the fixed array is refused with
     GEMM_E_SCRATCH before any device call (so this runs without a GPU)."""
