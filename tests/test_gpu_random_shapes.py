@@ -21,7 +21,7 @@ SIXTEEN_BIT_TILES = [1, 2, 3, 4, 5, 6, 7, 12, 13]
 FP8_TILES = [8, 9, 10]
 
 
-def cases(n=60, seed=20261202):
+def cases(n=200, seed=20261202):
     rng = random.Random(seed)
     out = []
     for i in range(n):
@@ -78,7 +78,7 @@ def test_random_problem_matches_the_oracle(tcg, case):
 SENTINEL = 0x5A5A
 
 
-def wide_cases(n=60, seed=20261203):
+def wide_cases(n=120, seed=20261203):
     """Batches of up to 3 items, sides up to 1200 (many ragged trips on every
     tile), the stage and split flags, operands shifted off 16-byte alignment
     (the element-copy path), and guard bands around C whose length also
@@ -126,7 +126,7 @@ def test_wide_random_problem_matches_the_oracle(tcg, case):
     check_against_oracle(w, A, B, C, bias=b)
 
 
-def split_cases(n=40, seed=20261204):
+def split_cases(n=100, seed=20261204):
     """Explicit K splits of 2 to 16 ranges (the reduction applies the bias,
     the activation and the output rounding), on any tile, batches of up to
     2 items."""
