@@ -32,7 +32,8 @@ timed step against it (timed_output_check).
 units' sustained rate on N(0, 1) bf16 or FP8 operands and the clock they run
 at); --copy-issue-cost: MFMA loops with global->LDS copies in between;
 --planner-sweep: the planner's plan, the autotuner's and torch.matmul on a
-sweep of shapes.
+sweep of shapes; --k-sweep: the headline's tile with 2 to 64 trips, split
+into a per-trip and a fixed cost per launch.
 """
 from __future__ import annotations
 
@@ -94,6 +95,9 @@ def parse():
     ap.add_argument("--copy-issue-cost", action="store_true",
                     help="instead of the GEMM: MFMA loops with global->LDS copies in between "
                          "(tcg_probe_copy_issue), cycles per MFMA per SIMD for each pattern")
+    ap.add_argument("--k-sweep", action="store_true",
+                    help="instead of the bench line: the headline's tile on 4096 x 4096 x K for "
+                         "K = 128 .. 4096, with a line through time and shader cycles per trip")
     ap.add_argument("--planner-sweep", action="store_true",
                     help="instead of the bench line: for a sweep of bf16 relu shapes, time the "
                          "planner's choice, the autotuner's and torch.matmul (one JSON line each)")
@@ -157,6 +161,75 @@ def planner_sweep():
         torch.cuda.empty_cache()
 
 
+# K of the K sweep: the headline's 4096 x 4096 output on its own tile, with
+# 2 to 64 trips of 64.
+KSWEEP = [128, 256, 512, 1024, 2048, 3072, 4096]
+
+
+def k_sweep(args):
+    """The headline's plan (tile 1: 256 x 256 x 64, two slots) on 4096 x 4096
+    x K for each K in KSWEEP: bf16 operands from N(0, 1), relu, bf16 out.
+    Per K: launches back to back for about a second (the shader clock
+    settles), then args.steps timed launches between two events on the
+    launch stream, with the clock probe around them.  Least-squares lines
+    through (trips, time per launch) and (trips, shader cycles per launch)
+    split a launch into a cost per trip and a fixed cost (the prologue, the
+    epilogue with its 32 MiB of stores, and the gap between launches)."""
+    import numpy as np
+    import torch
+
+    import tensor_core_gemm_amd as tcg
+
+    M = N = 4096
+    g = torch.Generator(device="cuda").manual_seed(3)
+    stream = torch.cuda.current_stream()
+    clock = make_clock_probe()
+    rows = []
+    for K in KSWEEP:
+        A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        B = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+        C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        plan = tcg.gemm_plan(tcg.make_desc(M, N, K, tcg.BF16, tcg.BF16, tcg.EPI_RELU, 0, tile=1))
+
+        def step():
+            tcg.gemm_run(plan, A, B, C, stream)
+
+        step()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t) / 20
+        for _ in range(max(100, int(1.0 / per))):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        clock.mark(0, stream)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        clock.mark(1, stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        mhz = clock.result()["mean_mhz"]
+        rows.append({"K": K, "trips": K // 64, "us": round(us, 3), "clock_mhz": mhz,
+                     "kcycles": round(us * mhz / 1e3, 2), "tflops": round(2.0 * M * N * K / us / 1e6, 1)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del A, B, C
+    trips = np.array([r["trips"] for r in rows], dtype=np.float64)
+    slope_us, fixed_us = np.polyfit(trips, np.array([r["us"] for r in rows]), 1)
+    slope_kc, fixed_kc = np.polyfit(trips, np.array([r["kcycles"] for r in rows]), 1)
+    print(json.dumps({
+        "metric": "time and shader cycles per launch against trips (bf16 4096 x 4096 x K, relu, tile 1)",
+        "steps": args.steps, "points": rows,
+        "fit_us": {"per_trip": round(float(slope_us), 4), "fixed": round(float(fixed_us), 3)},
+        "fit_kcycles": {"per_trip": round(float(slope_kc), 4), "fixed": round(float(fixed_kc), 3)},
+        "mfma_kcycles_per_trip": 2.048,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -175,6 +248,9 @@ def main():
     tcg.check_runtime()
     if args.planner_sweep:
         planner_sweep()
+        return
+    if args.k_sweep:
+        k_sweep(args)
         return
     if args.mfma_ceiling:
         mfma_ceiling(args)
