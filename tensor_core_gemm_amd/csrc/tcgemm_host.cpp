@@ -276,7 +276,7 @@ void choose(const gemm_desc& d, const gemm_device_caps& caps, bool may_split, in
 // run unsplit, and the rest as a second launch whose K is split so that it
 // occupies more CUs.  Taken where the time model estimates it at least 3 %
 // faster than one launch; the model's figures tracked measured ones on the
-// 256 x 256 tile (bf16, one box; one launch against head + split tail):
+// 256 x 256 tile (bf16, one machine; one launch against head + split tail):
 // 6144^3 402 against 370 us (tail 768 rows in 3 ranges), 4608^3 191 against
 // 171, 7168^3 630 against 558 (256 rows in 8), while 5120^3 (a last round
 // of 144 of 256 tiles) and 5120 x 5120 x 2048 lose, as estimated.
