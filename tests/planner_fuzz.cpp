@@ -10,14 +10,20 @@
 // run arguments and tune-cache text, and feeds them to every host entry
 // point.  Any sanitizer report aborts the process; the harness itself
 // checks a few invariants of the plans and the launch arguments and exits
-// non-zero on a violation.
+// non-zero on a violation.  With a thread count (third argument) the same
+// loop runs on that many threads at once, each with its own generator, so
+// that a ThreadSanitizer build sees the planner, the run entry points and
+// the tune cache used concurrently.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
+#include <thread>
+#include <vector>
 
 #include "tcgemm.h"
 #include "tcgemm_kernel_args.h"
@@ -25,9 +31,10 @@
 
 // ---------------------------------------------------------------------------
 // Stubs of the HIP runtime calls the host code makes.
-static bool g_device = false;  // pretend a gfx950 is present
-static long g_launches = 0;
-static int g_failures = 0;
+static thread_local bool g_device = false;  // pretend a gfx950 is present
+static std::atomic<long> g_launches{0};
+static std::atomic<int> g_failures{0};
+static uint64_t next();
 
 #define FAIL(...)                         \
   do {                                    \
@@ -72,7 +79,7 @@ hipError_t hipEventDestroy(hipEvent_t e) {
 hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
 hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) {
-  *ms = 0.1f + (float)(rand() % 100) * 0.001f;
+  *ms = 0.1f + (float)(next() % 100) * 0.001f;
   return hipSuccess;
 }
 const char* hipGetErrorString(hipError_t) { return "stub"; }
@@ -134,7 +141,7 @@ hipError_t launch_splitk_reduce(const RArgs& r, hipStream_t) {
 }  // namespace tcg
 
 // ---------------------------------------------------------------------------
-static uint64_t g_rng = 0x9E3779B97F4A7C15ull;
+static thread_local uint64_t g_rng = 0x9E3779B97F4A7C15ull;
 static uint64_t next() {
   g_rng ^= g_rng << 13;
   g_rng ^= g_rng >> 7;
@@ -255,12 +262,12 @@ static void try_runs(gemm_plan_t p, const gemm_desc& d) {
   (void)d;
 }
 
-int main(int argc, char** argv) {
-  const long iters = argc > 1 ? atol(argv[1]) : 20000;
-  const char* tmp = argc > 2 ? argv[2] : "/tmp/tcgemm_fuzz_cache.txt";
+// One thread's share of the iterations; tmp: its tune-cache file.
+static long fuzz_loop(long iters, const std::string& tmp_s, long offset) {
+  const char* tmp = tmp_s.c_str();
   long plans = 0;
   for (long it = 0; it < iters; ++it) {
-    g_device = (it % 2) == 1;
+    g_device = ((it + offset) % 2) == 1;
     gemm_desc d = draw_desc();
     gemm_device_caps c = draw_caps();
     gemm_plan_t p = nullptr;
@@ -279,6 +286,14 @@ int main(int argc, char** argv) {
     if (gemm_plan(&d, &p) == GEMM_OK) {
       try_runs(p, d);
       gemm_plan_destroy(p);
+    }
+    // the autotuner on stub launches and events (it fills the tune cache)
+    if (it % 53 == 0 && g_device) {
+      const uintptr_t base = (uintptr_t)1 << 44;
+      gemm_plan_t q = nullptr;
+      if (gemm_autotune(&d, (const void*)base, (const void*)(base + ((uintptr_t)1 << 42)),
+                        (void*)(base + ((uintptr_t)2 << 42)), nullptr, nullptr, &q) == GEMM_OK)
+        gemm_plan_destroy(q);
     }
     // the stage rule on random tiles
     int64_t tiles[3] = {(int64_t)(next() % 200000) - 8, (int64_t)(next() % 200000), (int64_t)(next() % 64)};
@@ -309,6 +324,7 @@ int main(int argc, char** argv) {
       }
       (void)gemm_tune_cache_load(tmp);
       (void)gemm_tune_cache_save(tmp);
+      (void)gemm_tune_cache_size();
       gemm_desc t = d;
       t.flags |= GEMM_FLAG_TUNED;
       gemm_plan_t q = nullptr;
@@ -316,9 +332,30 @@ int main(int argc, char** argv) {
       if (next() % 3 == 0) gemm_tune_cache_clear();
     }
   }
+  return plans;
+}
+
+int main(int argc, char** argv) {
+  const long iters = argc > 1 ? atol(argv[1]) : 20000;
+  const std::string tmp = argc > 2 ? argv[2] : "/tmp/tcgemm_fuzz_cache.txt";
+  const int threads = argc > 3 ? atoi(argv[3]) : 1;
+  long plans = 0;
+  if (threads <= 1) {
+    plans = fuzz_loop(iters, tmp, 0);
+  } else {
+    std::vector<std::thread> pool;
+    std::vector<long> counts(threads, 0);
+    for (int i = 0; i < threads; ++i)
+      pool.emplace_back([&, i]() {
+        g_rng = 0x9E3779B97F4A7C15ull ^ (0x100000001B3ull * (uint64_t)(i + 1));
+        counts[i] = fuzz_loop(iters / threads, tmp + "." + std::to_string(i), i);
+      });
+    for (auto& t : pool) t.join();
+    for (long c : counts) plans += c;
+  }
   gemm_tune_cache_clear();
   gemm_plan_destroy(nullptr);
-  printf("iterations %ld, plans %ld, stub launches %ld, invariant failures %d\n", iters, plans, g_launches,
-         g_failures);
-  return g_failures == 0 ? 0 : 1;
+  printf("iterations %ld, threads %d, plans %ld, stub launches %ld, invariant failures %d\n", iters, threads, plans,
+         g_launches.load(), g_failures.load());
+  return g_failures.load() == 0 ? 0 : 1;
 }

@@ -8,7 +8,9 @@ of tensor_core_gemm_amd/csrc/tcgemm_host.cpp (the planner, the run
 entry points' argument checks and launch-argument construction, the stage
 rule, the tune cache); its stub launchers check the grid and trip
 arithmetic the host hands each kernel.  Any sanitizer report or invariant
-violation fails the test.
+violation fails the test.  The same harness built under ThreadSanitizer runs
+its loop on eight threads at once (the planner's device-capability cache
+and the tune cache are shared by every thread of a process).
 """
 import os
 import subprocess
@@ -19,13 +21,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "tensor_core_gemm_amd", "csrc")
 
 
-@pytest.fixture(scope="module")
-def fuzz_bin(tmp_path_factory):
-    d = tmp_path_factory.mktemp("fuzz")
+def build_fuzz(d, sanitize):
     out = str(d / "planner_fuzz")
     flags = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__",
              "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-             "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+             *sanitize]
     for src, obj in ((os.path.join(CSRC, "tcgemm_host.cpp"), d / "host.o"),
                      (os.path.join(ROOT, "tests", "planner_fuzz.cpp"), d / "fuzz.o")):
         subprocess.run(["g++", *flags, "-x", "c++", "-c", src, "-o", str(obj)], check=True)
@@ -48,9 +48,19 @@ def fuzz_bin(tmp_path_factory):
         '  return gemm_run_ex(p, A, B, C, &a, s);\n'
         '}\n')
     subprocess.run(["g++", *flags, "-c", str(stand_in), "-o", str(d / "noalloc.o")], check=True)
-    subprocess.run(["g++", *flags, str(d / "host.o"), str(d / "fuzz.o"), str(d / "noalloc.o"), "-o", out],
-                   check=True)
+    subprocess.run(["g++", *flags, str(d / "host.o"), str(d / "fuzz.o"), str(d / "noalloc.o"), "-pthread",
+                    "-o", out], check=True)
     return out
+
+
+@pytest.fixture(scope="module")
+def fuzz_bin(tmp_path_factory):
+    return build_fuzz(tmp_path_factory.mktemp("fuzz"), ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"])
+
+
+@pytest.fixture(scope="module")
+def fuzz_bin_tsan(tmp_path_factory):
+    return build_fuzz(tmp_path_factory.mktemp("fuzz_tsan"), ["-fsanitize=thread"])
 
 
 def test_host_entry_points_under_asan_and_ubsan(fuzz_bin, tmp_path):
@@ -62,5 +72,17 @@ def test_host_entry_points_under_asan_and_ubsan(fuzz_bin, tmp_path):
     assert r.returncode == 0, r.stderr[-4000:]
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
     # the run reached the launchers, so the argument paths were exercised
+    launches = int(r.stdout.split("stub launches ")[1].split(",")[0])
+    assert launches > 100
+
+
+def test_host_entry_points_from_threads_under_tsan(fuzz_bin_tsan, tmp_path):
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1:second_deadlock_stack=1")
+    r = subprocess.run([fuzz_bin_tsan, "16000", str(tmp_path / "cache.txt"), "8"], capture_output=True,
+                       text=True, env=env, timeout=600)
+    print(r.stdout[-2000:], r.stderr[-4000:])
+    assert r.returncode == 0, r.stderr[-4000:]
+    assert "ThreadSanitizer" not in r.stderr
+    assert "threads 8" in r.stdout
     launches = int(r.stdout.split("stub launches ")[1].split(",")[0])
     assert launches > 100
