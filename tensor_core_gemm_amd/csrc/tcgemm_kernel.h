@@ -6,7 +6,9 @@
 //
 //   STAGES = 2  two LDS slots: chunk t+1 is copied into slot (t+1) mod 2
 //               while slot t mod 2 feeds the MFMAs; one barrier per trip
-//               (page "Module Tolk.Stage", "Two stages");
+//               (page "Module Tolk.Stage", "Two stages"); tiles built for
+//               deeper rings take 3 or 4 slots the same way (page
+//               "gizml:tile", Program.stages);
 //   STAGES = 1  one slot: copy at the start of the trip, barrier, compute,
 //               barrier (the single-stage case of the same page);
 //   STAGES = 0  unstaged: every wave loads its fragments straight from
@@ -16,8 +18,8 @@
 //
 // Copies move 16 bytes per lane (VEC16: a buffer load that writes LDS
 // directly, gfx950's asynchronous global->LDS copy) or, for operands whose
-// rows are not 16-byte aligned, 8 element loads per lane followed by one
-// 16-byte LDS write.  Either way a lane owns the same LDS chunk positions,
+// rows are not 16-byte aligned, 16 bytes' worth of element loads per lane
+// (8 16-bit or 16 FP8 elements) followed by one 16-byte LDS write.  Either way a lane owns the same LDS chunk positions,
 // so the LDS image is the same.
 //
 // Out-of-range elements read 0 (page "gizml:tile", In.at): masked lanes use
