@@ -98,6 +98,8 @@ def parse():
     ap.add_argument("--k-sweep", action="store_true",
                     help="instead of the bench line: the headline's tile on 4096 x 4096 x K for "
                          "K = 128 .. 4096, with a line through time and shader cycles per trip")
+    ap.add_argument("--sweep-dtype", choices=["bf16", "fp8"], default="bf16",
+                    help="--k-sweep operands: bf16 on tile 1, or FP8 E4M3 on tile 8 (K = 256 .. 8192)")
     ap.add_argument("--planner-sweep", action="store_true",
                     help="instead of the bench line: for a sweep of bf16 relu shapes, time the "
                          "planner's choice, the autotuner's and torch.matmul (one JSON line each)")
@@ -161,14 +163,16 @@ def planner_sweep():
         torch.cuda.empty_cache()
 
 
-# K of the K sweep: the headline's 4096 x 4096 output on its own tile, with
-# 2 to 64 trips of 64.
-KSWEEP = [128, 256, 512, 1024, 2048, 3072, 4096]
+# Trips of the K sweep: the headline's 4096 x 4096 output on its own tile,
+# with 2 to 64 trips (of 64 for bf16, of 128 for FP8).
+KSWEEP_TRIPS = [2, 4, 8, 16, 32, 48, 64]
 
 
 def k_sweep(args):
     """The headline's plan (tile 1: 256 x 256 x 64, two slots) on 4096 x 4096
-    x K for each K in KSWEEP: bf16 operands from N(0, 1), relu, bf16 out.
+    x K for K = 64 x KSWEEP_TRIPS: bf16 operands from N(0, 1), relu, bf16 out
+    (with --sweep-dtype fp8: FP8 E4M3 operands on tile 8, 256 x 256 x 128,
+    K = 128 x KSWEEP_TRIPS).
     Per K: launches back to back for about a second (the shader clock
     settles), then args.steps timed launches between two events on the
     launch stream, with the clock probe around them.  Least-squares lines
@@ -180,16 +184,21 @@ def k_sweep(args):
 
     import tensor_core_gemm_amd as tcg
 
+    import gemm_workloads as gw
+
     M = N = 4096
+    fp8 = args.sweep_dtype == "fp8"
+    in_dtype, tile, bk = (gw.FP8, 8, 128) if fp8 else (gw.BF16, 1, 64)
     g = torch.Generator(device="cuda").manual_seed(3)
     stream = torch.cuda.current_stream()
     clock = make_clock_probe()
     rows = []
-    for K in KSWEEP:
-        A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
-        B = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+    for trips in KSWEEP_TRIPS:
+        K = bk * trips
+        A = gw.draw((M, K), gw.NORMAL, in_dtype, g)
+        B = gw.draw((K, N), gw.NORMAL, in_dtype, g)
         C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
-        plan = tcg.gemm_plan(tcg.make_desc(M, N, K, tcg.BF16, tcg.BF16, tcg.EPI_RELU, 0, tile=1))
+        plan = tcg.gemm_plan(tcg.make_desc(M, N, K, in_dtype, tcg.BF16, tcg.EPI_RELU, 0, tile=tile))
 
         def step():
             tcg.gemm_run(plan, A, B, C, stream)
@@ -214,7 +223,7 @@ def k_sweep(args):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / args.steps * 1e3
         mhz = clock.result()["mean_mhz"]
-        rows.append({"K": K, "trips": K // 64, "us": round(us, 3), "clock_mhz": mhz,
+        rows.append({"K": K, "trips": trips, "us": round(us, 3), "clock_mhz": mhz,
                      "kcycles": round(us * mhz / 1e3, 2), "tflops": round(2.0 * M * N * K / us / 1e6, 1)})
         print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
         del A, B, C
@@ -222,7 +231,8 @@ def k_sweep(args):
     slope_us, fixed_us = np.polyfit(trips, np.array([r["us"] for r in rows]), 1)
     slope_kc, fixed_kc = np.polyfit(trips, np.array([r["kcycles"] for r in rows]), 1)
     print(json.dumps({
-        "metric": "time and shader cycles per launch against trips (bf16 4096 x 4096 x K, relu, tile 1)",
+        "metric": f"time and shader cycles per launch against trips ({args.sweep_dtype} 4096 x 4096 x K, "
+                  f"relu, tile {tile})",
         "steps": args.steps, "points": rows,
         "fit_us": {"per_trip": round(float(slope_us), 4), "fixed": round(float(fixed_us), 3)},
         "fit_kcycles": {"per_trip": round(float(slope_kc), 4), "fixed": round(float(fixed_kc), 3)},
