@@ -153,6 +153,18 @@ def test_split_k_with_bias_activation_batch_and_ragged_n(tcg):
     assert np.array_equal(as_bits(C), as_bits(Cu))
 
 
+def test_split_k_tanh_output_where_the_sum_cancels(tcg):
+    # a random split problem whose output (268, 88) cancels to about 0.0103
+    # against s = 44: the tolerance's floor carried through tanh's slope
+    # admits the oracle's own fold error there (test_tolerance.py)
+    w = gw.custom(516, 165, 1958, F16, F16, EPI_TANH, gw.NORMAL, seed=5471)
+    A, B = gw.make_inputs(w)
+    bias = gw.draw_bias(w.N, gw.NORMAL, seed=6471)
+    C, _, p = run(tcg, A, B, w, tile=3, split_k=8, bias=bias)
+    assert p.info().split_k == 8
+    check_against_oracle(w, A, B, C, bias=bias)
+
+
 def test_split_k_larger_than_the_trips_is_capped(tcg):
     w = gw.custom(70, 90, 100, F16, F32, EPI_NONE, gw.INT4, seed=73)
     A, B = gw.make_inputs(w)
