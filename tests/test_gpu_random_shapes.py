@@ -4,7 +4,9 @@ Sizes from 1 to ~700 on every side (K from 0), ragged against every tile,
 operands fp16, bf16 or FP8, outputs fp32, fp16 or bf16, every activation,
 with and without a bias row, on the planner's choice or on an explicit tile
 (the persistent short-K tile where its limits allow).  Integer inputs must
-match exactly; Gaussian ones within the relative tolerance.
+match exactly; Gaussian ones within the relative tolerance.  Larger problems
+(sides up to 8192, the planner with split K allowed) are checked on sampled
+outputs.
 """
 import random
 
@@ -13,7 +15,7 @@ import torch
 
 import gemm_workloads as gw
 from gemm_workloads import BF16, F16, F32, FP8
-from gpu_helpers import check_against_oracle, run
+from gpu_helpers import check_against_oracle, check_sampled, note, run
 
 pytestmark = pytest.mark.gpu
 
@@ -161,3 +163,43 @@ def test_split_random_problem_matches_the_oracle(tcg, case):
     # the planner keeps ranges of whole trips: at most `split` of them
     assert 1 <= info.split_k <= split
     check_against_oracle(w, A, B, C, bias=b)
+
+
+def large_cases(n=40, seed=20261205):
+    """Sides from 1000 to 8192 (several rounds of tiles on every tile size,
+    small last rounds), the planner's plan with split K allowed on most (so
+    whole-problem splits and split tails), every operand and output type and
+    activation, bias rows on some."""
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        in_dtype = rng.choice([F16, BF16, FP8])
+        out_dtype = rng.choice([F32, F16, BF16])
+        M = rng.randint(1000, 8192)
+        N = rng.choice([rng.randint(1000, 8192), 8 * rng.randint(125, 1024)])
+        K = rng.choice([rng.randint(1, 8192), 64 * rng.randint(1, 128)])
+        epi = rng.choice([0, 1, 1, 2, 3, 4, 5])
+        bias = rng.random() < 0.3
+        dist = gw.INT4 if (rng.random() < 0.3 and epi in (0, 1) and not bias) else gw.NORMAL
+        split = rng.random() < 0.7
+        out.append((i, M, N, K, in_dtype, out_dtype, epi, bias, dist, split))
+    return out
+
+
+@pytest.mark.parametrize("case", large_cases(), ids=lambda c: f"large{c[0]}")
+def test_large_random_problem_matches_the_oracle_on_samples(tcg, case):
+    i, M, N, K, in_dtype, out_dtype, epi, bias, dist, split = case
+    w = gw.custom(M, N, K, in_dtype, out_dtype, epi, dist, seed=7000 + i)
+    g = torch.Generator(device="cuda").manual_seed(7000 + i)
+    A = gw.draw((M, K), dist, in_dtype, g)
+    B = gw.draw((K, N), dist, in_dtype, g)
+    b = gw.draw_bias(N, gw.NORMAL, seed=8000 + i) if bias else None
+    flags = (tcg.FLAG_SPLIT_K if split else 0) | (tcg.FLAG_BIAS if bias else 0)
+    p = tcg.gemm_plan(tcg.make_desc(M, N, K, in_dtype, out_dtype, epi, flags))
+    note(f"large{i}: {M}x{N}x{K}: {p.describe()}")
+    C = torch.full((M, N), float("nan"), dtype=gw.TORCH_DTYPE[out_dtype], device="cuda")
+    wsb = p.info().workspace_bytes
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+    tcg.gemm_run_ex(p, A, B, C, bias=b.cuda() if bias else None, workspace=ws)
+    torch.cuda.synchronize()
+    check_sampled(w, A.cpu(), B.cpu(), C.cpu().reshape(1, M, N), count=2048, seed=i, bias=b)
