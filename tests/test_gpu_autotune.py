@@ -158,3 +158,41 @@ def test_a_restricted_search_answers_without_caching(tcg):
     tcg.gemm_run_ex(p3, Ad, Bd, C, workspace=ws)
     torch.cuda.synchronize()
     check_against_oracle(w, A, B, C.cpu().reshape(1, M, N))
+
+
+def _tune_cases(n=24, seed=20261206):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        in_dtype = rng.choice([F16, BF16, gw.FP8])
+        out_dtype = rng.choice([F32, F16, BF16])
+        M, N, K = rng.randint(1, 1500), rng.randint(1, 1500), rng.randint(1, 3000)
+        epi = rng.choice([0, 1, 2, 3, 4, 5])
+        bias = rng.random() < 0.3
+        dist = gw.INT4 if (rng.random() < 0.4 and epi in (0, 1) and not bias) else gw.NORMAL
+        out.append((i, M, N, K, in_dtype, out_dtype, epi, bias, dist))
+    return out
+
+
+@pytest.mark.parametrize("case", _tune_cases(), ids=lambda c: f"tune{c[0]}")
+def test_random_problem_tuned_then_replayed_matches_the_oracle(tcg, case):
+    """gemm_autotune with split K allowed and a workspace, then the cached
+    choice through GEMM_FLAG_TUNED, every output against the oracle."""
+    i, M, N, K, in_dtype, out_dtype, epi, bias, dist = case
+    w = gw.custom(M, N, K, in_dtype, out_dtype, epi, dist, seed=9000 + i)
+    A, B = gw.make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    b = gw.draw_bias(N, gw.NORMAL, seed=9500 + i) if bias else None
+    bd = b.cuda() if bias else None
+    flags = tcg.FLAG_SPLIT_K | (tcg.FLAG_BIAS if bias else 0)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    C = torch.empty((M, N), dtype=gw.TORCH_DTYPE[out_dtype], device="cuda")
+    tcg.gemm_autotune(tcg.make_desc(M, N, K, in_dtype, out_dtype, epi, flags), Ad, Bd, C, bias=bd,
+                      workspace=ws)
+    p = tcg.gemm_plan(tcg.make_desc(M, N, K, in_dtype, out_dtype, epi, flags | tcg.FLAG_TUNED))
+    note(f"tuned {w.name}: {p.describe()}")
+    C.fill_(float("nan"))
+    tcg.gemm_run_ex(p, Ad, Bd, C, bias=bd, workspace=ws if p.info().workspace_bytes else None)
+    torch.cuda.synchronize()
+    check_against_oracle(w, A, B, C.cpu().reshape(1, M, N), bias=b)
