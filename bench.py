@@ -568,24 +568,29 @@ def torch_matmul_time(w, io, warmup, steps, stream):
         if w.epilogue:
             torch.relu_(y)
 
+    clock = make_clock_probe()
+
     def timed(fn):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        clock.mark(0, stream)
         for _ in range(steps):
             fn()
+        clock.mark(1, stream)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
+        return (time.perf_counter() - t0) * 1e3 / steps, clock.result()["mean_mhz"]
 
-    ms = timed(step)
+    ms, mhz = timed(step)
     out = {"ms_per_step": round(ms, 5), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2),
-           "with_relu": bool(w.epilogue)}
+           "with_relu": bool(w.epilogue), "clock_mhz_measured": mhz}
     if w.epilogue:
         # the product alone, without the separate relu
-        ms_gemm = timed(gemm)
+        ms_gemm, mhz_gemm = timed(gemm)
         out["gemm_only_ms"] = round(ms_gemm, 5)
         out["gemm_only_tflops"] = round(w.flops / (ms_gemm * 1e-3) / 1e12, 2)
+        out["gemm_only_clock_mhz_measured"] = mhz_gemm
     return out
 
 
