@@ -143,3 +143,42 @@ def test_special_values_match_the_oracle(tcg, path, in_dtype, out_dtype, epi):
     if in_dtype == BF16 and out_dtype == F32:
         assert np.isfinite(want[7, 8]) and want[7, 8] > 3.39e38
     compare(got, want, epi, f"{path} in={in_dtype} out={out_dtype} epi={epi}")
+
+
+# (name, input type, output type, a, b, K): every value exact, so one result.
+SUBNORMAL = [
+    ("fp16 subnormal A", F16, F32, 2.0 ** -20, 2.0 ** 10, 64),
+    ("fp16 subnormal A and B", F16, F32, 2.0 ** -20, 2.0 ** -16, 64),
+    ("fp16 subnormal output", F16, F16, 2.0 ** -14, 2.0 ** -10, 64),
+    ("bf16 subnormal A", BF16, F32, 2.0 ** -130, 2.0 ** 100, 64),
+    ("fp32 subnormal output", BF16, F32, 2.0 ** -70, 2.0 ** -70, 64),
+    ("bf16 subnormal output", BF16, BF16, 2.0 ** -70, 2.0 ** -65, 64),
+    ("fp8 subnormal A", gw.FP8, F32, 2.0 ** -8, 2.0, 128),
+    ("fp8 subnormal A and B", gw.FP8, F32, 2.0 ** -8, 2.0 ** -9, 128),
+]
+
+
+@pytest.mark.parametrize("name,in_dtype,out_dtype,a,b,K", SUBNORMAL, ids=[c[0] for c in SUBNORMAL])
+def test_subnormal_operands_and_outputs_are_kept(tcg, name, in_dtype, out_dtype, a, b, K):
+    """Subnormal operands and subnormal results are values like any other
+    (gizml:tile, Tile.to: the value a store and a load of the type give): the
+    MFMA and the epilogue keep them, staged and unstaged, bit for bit equal
+    to the oracle's."""
+    M = N = 64
+    tdt = gw.TORCH_DTYPE[in_dtype]
+    A = torch.full((M, K), a, dtype=torch.float32)
+    A[::2] *= 3.0  # two row values, both still exact
+    A, B = A.to(tdt), torch.full((K, N), b, dtype=torch.float32).to(tdt)
+    want = oracle.gemm(A, B, M, N, K, in_dtype, out_dtype, EPI_NONE).reshape(M, N)
+    wbits = want.view(np.int32) if out_dtype == F32 else want.view(np.int16)
+    for flags in (0, tcg.FLAG_UNSTAGED):
+        w = gw.custom(M, N, K, in_dtype, out_dtype, EPI_NONE, gw.NORMAL, seed=0)
+        C, _, p = run(tcg, A, B, w, flags=flags)
+        note(f"{name}: {p.describe()}")
+        got = C.reshape(M, N).view(torch.int32 if out_dtype == F32 else torch.int16).numpy()
+        assert np.array_equal(got, wbits), (name, flags)
+    # the case is what its name says
+    y = oracle.to_float(out_dtype, want)[1, 0]
+    tiny = {F32: 2.0 ** -126, F16: 2.0 ** -14, BF16: 2.0 ** -126}[out_dtype]
+    if "output" in name:
+        assert 0 < y < tiny, (name, y)
