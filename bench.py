@@ -399,6 +399,10 @@ def main():
             "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
+            # context only: the same fraction against the peak at the shader clock measured over the
+            # timed region (the MFMA peak scales with the clock; the chip ran below 2.4 GHz)
+            "frac_at_measured_clock": (round(achieved / (peak * clock_measured["mean_mhz"] / (caps.clock_khz / 1000)), 4)
+                                       if bound == "mfma" and clock_measured.get("mean_mhz") else None),
             "kernel_avg_ms": round(avg_launch_ms, 5),
             "launch_ms": per_launch,
             "flops_per_launch": flops,
