@@ -151,4 +151,49 @@ TCG_HD constexpr int b_frag_row(int s, int h) {
   return ES == 2 ? 16 * s + 4 * h : 64 * s + 8 * h;
 }
 
+// ---------------------------------------------------------------------------
+// The persistent short-K tile (tile 11, 16-bit operands, K <= 96, N <= 288).
+//
+// An A slot holds shortk::kBM rows of shortk::kCprA = 12 chunks.  Twelve is
+// not a power of two, so the XOR is bounded by the row's groups of four
+// chunks: chunk c of row r sits at position c ^ ((r / 4) mod 4), which stays
+// inside c's group.  Rows are 192 bytes apart, so four consecutive rows
+// start on four different 64-byte ranges of a 256-byte line and the XOR
+// separates the four such quads that 16 lanes of a 16-byte read cover.
+TCG_HD constexpr int swz_shortk_a(int r) { return (r >> 2) & 3; }
+// Copy plan: position P of an A slot receives logical chunk (r, c).
+TCG_HD constexpr ChunkRC shortk_a_chunk_at(int P) {
+  const int r = P / shortk::kCprA;
+  return ChunkRC{r, (P % shortk::kCprA) ^ swz_shortk_a(r)};
+}
+// Byte offset, inside the slot, of the A fragment of k-step s for wave w:
+// row 32 w + (lane mod 32), logical chunk 2 s + lane / 32 (8 k-contiguous
+// values, the MFMA operand layout of the 16-bit tiles above).
+TCG_HD constexpr int shortk_a_frag(int lane, int s, int w) {
+  const int r = 32 * w + (lane & 31);
+  return r * (shortk::kCprA * 16) + 16 * ((2 * s + (lane >> 5)) ^ swz_shortk_a(r));
+}
+// B is copied row-major and unswizzled (K rows of shortk::kCprB * 16 = 576
+// bytes; 576 mod 256 = 64, so the four rows of a transposing read fall on
+// four different 64-byte bank ranges).  Lane's transposing read h (h = 0, 1)
+// of the fragment of MFMA block j at k-step s: as in b_frag_base, lane
+// 4 e + q of a 16-lane group reads row e of the group's 4 x 16 block at
+// columns 4 q .. 4 q + 3; the block's rows start at 16 s + 8 (lane / 32)
+// + 4 h, its columns at 32 j + 16 ((lane / 16) mod 2).  The byte offset is
+// shortk_b_frag_base(lane) + shortk_b_frag_step(j, s, h): the lane's part
+// and a part that the unrolled loops make a constant.
+TCG_HD constexpr int shortk_b_frag_base(int lane) {
+  const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return r * (shortk::kCprB * 16) + 2 * col;
+}
+TCG_HD constexpr int shortk_b_frag_step(int j, int s, int h) {
+  return (16 * s + 4 * h) * (shortk::kCprB * 16) + 2 * 32 * j;
+}
+// The fragment image that replaces B after those reads: fragment f (block
+// j, k-step s: f = j * KS + s) is kShortkFragBytes with lane l's 16 bytes
+// at shortk_image_lane(l), i.e. offset shortk_image_lane(l) + f * kShortkFragBytes.
+constexpr int kShortkFragBytes = 1024;
+TCG_HD constexpr int shortk_image_lane(int lane) { return lane * 16; }
+
 }  // namespace tcg

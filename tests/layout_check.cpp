@@ -77,3 +77,34 @@ extern "C" int layout_tile_count(void) { return tcg::kNumTiles; }
 extern "C" int layout_query(int tile, int what, int a0, int a1, int a2, int a3, int* out) {
   return dispatch<1>(tile, what, a0, a1, a2, a3, out);
 }
+
+// The persistent short-K tile's own layout (the shortk_* functions).
+extern "C" int layout_shortk_query(int what, int a0, int a1, int a2, int a3, int* out) {
+  namespace sk = tcg::shortk;
+  switch (what) {
+    case 0: {  // A copy map: out[2P], out[2P+1] = (r, c) for P < kBM * kCprA
+      const int n = sk::kBM * sk::kCprA;
+      for (int P = 0; P < n; ++P) {
+        const tcg::ChunkRC rc = tcg::shortk_a_chunk_at(P);
+        out[2 * P] = rc.r;
+        out[2 * P + 1] = rc.c;
+      }
+      return n;
+    }
+    case 1:  // A fragment offset: lane a0, k-step a1, wave a2
+      out[0] = tcg::shortk_a_frag(a0, a1, a2);
+      return 1;
+    case 2:  // B transposing read offset: lane a0, block a1, k-step a2, read a3
+      out[0] = tcg::shortk_b_frag_base(a0) + tcg::shortk_b_frag_step(a1, a2, a3);
+      return 1;
+    case 3:  // fragment image offset: lane a0, fragment a1
+      out[0] = a1 * tcg::kShortkFragBytes + tcg::shortk_image_lane(a0);
+      return 1;
+    case 4:  // geometry: kBM, kCprA, kCprB, kFN, kKS, kBBytes, kCopiesA, kShortkFragBytes
+      out[0] = sk::kBM; out[1] = sk::kCprA; out[2] = sk::kCprB; out[3] = sk::kFN; out[4] = sk::kKS;
+      out[5] = sk::kBBytes; out[6] = sk::kCopiesA; out[7] = tcg::kShortkFragBytes;
+      return 8;
+    default:
+      return -1;
+  }
+}

@@ -42,7 +42,13 @@ def lay(tmp_path_factory):
         assert n >= 0
         return np.frombuffer(buf, dtype=np.int32, count=2 * n if what <= 1 else n).copy()
 
+    def sk(what, a0=0, a1=0, a2=0, a3=0):
+        n = lib.layout_shortk_query(what, a0, a1, a2, a3, buf)
+        assert n >= 0
+        return np.frombuffer(buf, dtype=np.int32, count=2 * n if what == 0 else n).copy()
+
     q.count = lib.layout_tile_count()
+    q.shortk = sk
     return q
 
 
@@ -52,7 +58,7 @@ def tiles(lay):
         g = lay(t, 4)
         keys = ("ES", "CPR_A", "CPR_B", "WM", "WN", "WTM", "WTN", "MK", "BM", "BN", "BK", "persistent")
         d = dict(zip(keys, g.tolist()))
-        if not d["persistent"]:  # tile 11 has its own LDS image (tcgemm_shortk.hip)
+        if not d["persistent"]:  # tile 11 has its own layout (the short-K tests below)
             out.append((t, d))
     return out
 
@@ -66,7 +72,8 @@ def inverse_copy_map(lay, t, operand, rows, cpr):
 
 
 def test_every_configuration_is_covered(lay):
-    assert len(tiles(lay)) == lay.count - 1  # all but the persistent short-K tile
+    # all but the persistent short-K tile, whose layout the short-K tests cover
+    assert len(tiles(lay)) == lay.count - 1
 
 
 def test_copy_plan_is_a_bijection_onto_the_tile(lay):
@@ -192,3 +199,113 @@ def test_a_mutated_swizzle_fails_the_bank_model(lay, tmp_path):
         return len(banks)
     assert pairs_for(8, lambda r: (2 * (r & 7)) & 7) == 4
     assert pairs_for(8, lambda r: (2 * ((r >> 1) & 7)) & 7) == 8
+
+
+# ---------------------------------------------------------------------------
+# The persistent short-K tile (tile 11): an A slot of 128 rows of 12 chunks
+# with the XOR (r / 4) mod 4, an unswizzled row-major B tile read with the
+# transposing reads, and the fragment image that then replaces B.
+
+def _shortk_geometry(lay):
+    keys = ("BM", "CPR_A", "CPR_B", "FN", "KS", "B_BYTES", "COPIES_A", "FRAG_BYTES")
+    return dict(zip(keys, lay.shortk(4).tolist()))
+
+
+def _shortk_positions(lay, g):
+    rc = lay.shortk(0).reshape(-1, 2)
+    pos = -np.ones((g["BM"], g["CPR_A"]), np.int64)
+    for P, (r, c) in enumerate(rc):
+        pos[r, c] = P
+    return rc, pos
+
+
+def test_short_k_copy_plan_is_a_bijection_onto_the_slot(lay):
+    g = _shortk_geometry(lay)
+    assert g["CPR_A"] == 12 and g["BM"] * g["CPR_A"] == g["COPIES_A"] * 256  # whole copy rounds
+    rc, pos = _shortk_positions(lay, g)
+    n = g["BM"] * g["CPR_A"]
+    assert len(rc) == n and (pos >= 0).all()
+    assert np.array_equal(np.sort(rc[:, 0] * g["CPR_A"] + rc[:, 1]), np.arange(n))
+    P = np.arange(n)
+    assert np.array_equal(rc[:, 0], P // g["CPR_A"])  # positions fill rows in order
+    # the XOR keeps every chunk inside its group of four (12 is not a power of two)
+    assert np.array_equal(rc[:, 1] // 4, (P % g["CPR_A"]) // 4)
+
+
+def test_short_k_a_fragment_reads_hit_their_chunks(lay):
+    g = _shortk_geometry(lay)
+    _, pos = _shortk_positions(lay, g)
+    for w in range(4):
+        for s in range(g["KS"]):
+            for lane in range(64):
+                off = int(lay.shortk(1, lane, s, w)[0])
+                r, c = 32 * w + (lane & 31), 2 * s + (lane >> 5)
+                assert off % 16 == 0 and off // 16 == pos[r, c], (w, s, lane)
+
+
+def test_short_k_b_reads_transpose_into_each_lanes_column(lay):
+    """B sits row-major in LDS (rows of CPR_B chunks, no swizzle).  Under
+    ds_read_b64_tr_b16's lane permutation (lane x of a 16-lane group gets
+    element x mod 4 of the reads of lanes 4e + x/4), lane l must receive
+    column 32j + (l mod 32) at rows 16s + 8(l/32) + 4h + e, e = 0..3."""
+    g = _shortk_geometry(lay)
+    rb = g["CPR_B"] * 16
+    for j in range(g["FN"]):
+        for s in range(g["KS"]):
+            for h in range(2):
+                cover = {}
+                for lane in range(64):
+                    off = int(lay.shortk(2, lane, j, s, h)[0])
+                    assert off % 8 == 0 and 0 <= off and off + 8 <= g["B_BYTES"]
+                    cover[lane] = (off // rb, (off % rb) // 2)
+                for lane in range(64):
+                    g0, x = lane & ~15, lane & 15
+                    got = [(cover[g0 + 4 * e + x // 4][0], cover[g0 + 4 * e + x // 4][1] + x % 4)
+                           for e in range(4)]
+                    want = [(16 * s + 8 * (lane >> 5) + 4 * h + e, 32 * j + (lane & 31)) for e in range(4)]
+                    assert got == want, (j, s, h, lane)
+
+
+def test_short_k_fragment_image_fills_the_b_region_exactly(lay):
+    """The image is written over B in place: every fragment's 1 KiB, one
+    16-byte piece per lane, and together exactly the bytes of the B tile."""
+    g = _shortk_geometry(lay)
+    nf = g["FN"] * g["KS"]
+    offs = np.array([[int(lay.shortk(3, lane, f)[0]) for lane in range(64)] for f in range(nf)])
+    assert (offs % 16 == 0).all()
+    assert np.array_equal(np.sort(offs.ravel()), np.arange(0, g["B_BYTES"], 16))
+    assert nf * g["FRAG_BYTES"] == g["B_BYTES"]
+
+
+def test_short_k_reads_are_free_of_bank_conflicts(lay):
+    """Same bank model as above: 16 lanes of a 16-byte read need 16
+    different 16-byte bank groups, 32 lanes of an 8-byte read 64 banks."""
+    g = _shortk_geometry(lay)
+    for w in range(4):
+        for s in range(g["KS"]):
+            offs = np.array([int(lay.shortk(1, lane, s, w)[0]) for lane in range(64)])
+            for q in range(4):
+                assert len(set(((offs[16 * q:16 * q + 16] // 16) % 16).tolist())) == 16, ("A", w, s, q)
+    for j in range(g["FN"]):
+        for s in range(g["KS"]):
+            for h in range(2):
+                offs = np.array([int(lay.shortk(2, lane, j, s, h)[0]) for lane in range(64)])
+                for half in range(2):
+                    o = offs[32 * half:32 * half + 32]
+                    banks = ((o[:, None] + np.array([0, 4])[None, :]) // 4) % 64
+                    assert len(set(banks.ravel().tolist())) == 64, ("B", j, s, h, half)
+    for f in range(g["FN"] * g["KS"]):
+        offs = np.array([int(lay.shortk(3, lane, f)[0]) for lane in range(64)])
+        for q in range(4):
+            assert len(set(((offs[16 * q:16 * q + 16] // 16) % 16).tolist())) == 16, ("image", f, q)
+
+
+def test_short_k_model_rejects_an_unswizzled_a_slot(lay):
+    """The model has teeth here too: without the XOR, rows 192 bytes apart
+    put 16 lanes' 16-byte reads on only 4 different bank groups."""
+    g = _shortk_geometry(lay)
+    ra = g["CPR_A"] * 16
+    plain = [(r * ra + 16 * 0) // 16 % 16 for r in range(16)]
+    assert len(set(plain)) == 4
+    swizzled = [int(lay.shortk(1, lane, 0, 0)[0]) // 16 % 16 for lane in range(16)]
+    assert len(set(swizzled)) == 16
