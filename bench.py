@@ -87,9 +87,10 @@ def parse():
                     help="instead of the GEMM: the register-only MFMA loop (bf16 32x32x16, operands "
                          "drawn from N(0, 1)) on every CU, timed the same way (the throughput the "
                          "MFMA units sustain on this data with no memory traffic)")
-    ap.add_argument("--ceiling-dtype", choices=["bf16", "fp8"], default="bf16",
+    ap.add_argument("--ceiling-dtype", choices=["bf16", "bf16_16x16x32", "fp8"], default="bf16",
                     help="operand type of the --mfma-ceiling loop (fp8: v_mfma_f32_32x32x64_f8f6f4 "
-                         "with E4M3 operands)")
+                         "with E4M3 operands; bf16_16x16x32: the other bf16 shape, "
+                         "v_mfma_f32_16x16x32_bf16)")
     ap.add_argument("--ceiling-iters", type=int, default=0,
                     help="rounds of 64 MFMAs per wave in one --mfma-ceiling launch")
     ap.add_argument("--copy-issue-cost", action="store_true",
@@ -468,9 +469,16 @@ def mfma_ceiling(args):
     if fp8:
         ops = gw.draw((16 * 64 * 32,), gw.NORMAL, gw.FP8, gen).view(torch.uint8).cuda()
         kind, iters = probe.MFMA_32x32x64_FP8, args.ceiling_iters or 35
+        name = "v_mfma_f32_32x32x64_f8f6f4, E4M3"
+    elif args.ceiling_dtype == "bf16_16x16x32":
+        # half the flops per instruction: twice the rounds for the same work
+        ops = gw.draw((16 * 64 * 8,), gw.NORMAL, gw.BF16, gen).view(torch.int16).cuda()
+        kind, iters = probe.MFMA_16x16x32_BF16, args.ceiling_iters or 140
+        name = "v_mfma_f32_16x16x32_bf16, bf16"
     else:
         ops = gw.draw((16 * 64 * 8,), gw.NORMAL, gw.BF16, gen).view(torch.int16).cuda()
         kind, iters = probe.MFMA_32x32x16_BF16, args.ceiling_iters or 70
+        name = "v_mfma_f32_32x32x16_bf16, bf16"
     sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
     ticks = torch.zeros(wg, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
@@ -497,7 +505,6 @@ def mfma_ceiling(args):
     mfmas_per_wave = iters * 64
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[gw.FP8 if fp8 else gw.BF16]
-    name = ("v_mfma_f32_32x32x64_f8f6f4, E4M3" if fp8 else "v_mfma_f32_32x32x16_bf16, bf16")
     print(json.dumps({
         "metric": f"MFMA-only throughput, register operands ({name} operands from N(0,1))",
         "value": round(tflops, 2), "unit": "TFLOP/s", "frac_of_peak": round(tflops / peak, 4),
@@ -511,8 +518,11 @@ def mfma_ceiling(args):
 
 def copy_issue_cost():
     """Cycles per MFMA per SIMD of a register-only MFMA loop with and without
-    global->LDS copies between the MFMAs, with one and two waves per SIMD
-    (tcg_probe_copy_issue; median over the CUs, after 100 warm-up launches)."""
+    global->LDS copies between the MFMAs, with one and two waves per SIMD,
+    and for the 32x32x16 and the 16x16x32 bf16 shapes (tcg_probe_copy_issue;
+    median over the CUs).  Per pattern: 1000 warm-up launches, then 400
+    timed ones with HIP events and the shader clock measured around them,
+    so the rate under the power manager is reported beside the cycles."""
     import numpy as np
     import torch
 
@@ -526,17 +536,34 @@ def copy_issue_cost():
     src = torch.zeros(65536 // 4, dtype=torch.int32, device="cuda")
     sink = torch.empty(wg * 512, device="cuda")
     ticks = torch.zeros(wg, dtype=torch.int64, device="cuda")
-    iters = 400
+    stream = torch.cuda.current_stream()
+    clock = make_clock_probe()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    iters, timed = 400, 400
     out = {}
-    for pat, (name, _) in probe.COPY_PATTERNS.items():
-        for _ in range(100):
-            per_simd = probe.copy_issue(pat, wg, iters, ops, src, sink, ticks)
+    for pat, (name, waves, per_round) in probe.COPY_PATTERNS.items():
+        mflops = probe.COPY_PATTERN_MFMA_FLOPS[pat]
+        for _ in range(1000):
+            per_simd = probe.copy_issue(pat, wg, iters, ops, src, sink, ticks, stream)
         torch.cuda.synchronize()
-        cyc = ticks.cpu().numpy().astype(np.float64) / per_simd
-        out[name] = round(float(np.median(cyc)), 2)
-    print(json.dumps({"metric": "cycles per MFMA per SIMD (v_mfma_f32_32x32x16_bf16, register operands), "
+        clock.mark(0, stream)
+        e0.record(stream)
+        for _ in range(timed):
+            probe.copy_issue(pat, wg, iters, ops, src, sink, ticks, stream)
+        e1.record(stream)
+        clock.mark(1, stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / timed
+        cyc = float(np.median(ticks.cpu().numpy().astype(np.float64))) / per_simd
+        flops = wg * waves * iters * per_round * mflops
+        out[name] = {"cycles_per_mfma": round(cyc, 2),
+                     "cycles_per_32768_flops": round(cyc * 32768 / mflops, 2),
+                     "us_per_launch": round(ms * 1e3, 2),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "clock_mhz": clock.result()["mean_mhz"]}
+    print(json.dumps({"metric": "cycles per MFMA per SIMD (bf16 MFMAs on register operands from N(0,1)), "
                                 "with global->LDS copies between the MFMAs",
-                      "mfmas_per_round_per_wave": 32, "rounds": iters, "workgroups": wg,
+                      "flops_per_round_per_wave": 32 * 32768, "rounds": iters, "workgroups": wg,
                       "patterns": out}), flush=True)
 
 

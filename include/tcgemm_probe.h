@@ -137,20 +137,26 @@ enum {
   TCG_PROBE_COPY_4W_2X4 = 2,  /* 4 waves, 8 copies in 2 bursts of 4 */
   TCG_PROBE_COPY_8W_NONE = 3, /* 8 waves, no copies */
   TCG_PROBE_COPY_8W_4X1 = 4,  /* 8 waves, 4 copies each: the same copies per SIMD as pattern 1 */
-  TCG_PROBE_COPY_8W_8X1 = 5   /* 8 waves, 8 copies each: twice pattern 1's copies per SIMD */
+  TCG_PROBE_COPY_8W_8X1 = 5,  /* 8 waves, 8 copies each: twice pattern 1's copies per SIMD */
+  /* the same two loops as patterns 0 and 1 with 64 v_mfma_f32_16x16x32_bf16
+   * per round (the same flops and copies per round; one copy per 8 MFMAs) */
+  TCG_PROBE_COPY_4W_NONE_16X16 = 6,
+  TCG_PROBE_COPY_4W_8X1_16X16 = 7
 };
 
 /*
  * How long a global->LDS copy holds up MFMA issue: `workgroups` workgroups
  * (one per CU: each reserves 96 KiB of LDS) of 4 or 8 waves run `iters`
- * rounds of 32 back-to-back v_mfma_f32_32x32x16_bf16 per wave on register
- * operands, with the copies of `pattern` (TCG_PROBE_COPY_*) in between.
+ * rounds of 32 back-to-back v_mfma_f32_32x32x16_bf16 (or 64
+ * v_mfma_f32_16x16x32_bf16) per wave on register operands, with the copies
+ * of `pattern` (TCG_PROBE_COPY_*) in between.
  * operands_dev: [8][64][8] 16-bit values (A registers 0-3, B 4-7); src_dev:
  * 64 KiB of device memory the copies read (caller-owned); sink_dev: 512
  * floats per workgroup; ticks_dev: per workgroup, the shader-clock cycles
  * (s_memtime) of the loop, taken between two workgroup barriers so they
- * cover every wave.  Cycles per MFMA per SIMD = ticks / (iters * 32 * waves
- * per SIMD).  GEMM_E_ARG on a bad pattern, count or null pointer.
+ * cover every wave.  Cycles per MFMA per SIMD = ticks / (iters * R * waves
+ * per SIMD), R = 32 MFMAs per round (64 for the 16X16 patterns).
+ * GEMM_E_ARG on a bad pattern, count or null pointer.
  */
 int tcg_probe_copy_issue(int pattern, int workgroups, int iters, const uint16_t* operands_dev,
                          const uint32_t* src_dev, float* sink_dev, uint64_t* ticks_dev, void* stream);

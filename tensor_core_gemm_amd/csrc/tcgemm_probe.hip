@@ -262,13 +262,15 @@ __global__ __launch_bounds__(256) void probe_mfma_rate_kernel(const uint16_t* op
 // between two workgroup barriers, so it covers every wave.  Compared with
 // the copy-free loop, the time per MFMA shows how long a copy holds up the
 // MFMA issue of its wave, and how much a second wave on the SIMD hides.
+// With S16 the rounds are 64 v_mfma_f32_16x16x32_bf16 instead (the same
+// flops and the same copies per round, so one copy per 8 MFMAs).
 constexpr int kCopyProbeLds = 96 * 1024;
 
-template <int NWV, int NB, int BURST>
+template <int NWV, int NB, int BURST, bool S16>
 __global__ __launch_bounds__(NWV * 64) void probe_copy_issue_kernel(const uint16_t* ops, const uint32_t* src,
                                                                    int iters, float* sink, uint64_t* ticks) {
   __shared__ __attribute__((aligned(1024))) char lds[kCopyProbeLds];
-  constexpr int RM = 32;
+  constexpr int RM = S16 ? 64 : 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   u32x4 a[4], b[4];
 #pragma unroll
@@ -280,10 +282,14 @@ __global__ __launch_bounds__(NWV * 64) void probe_copy_issue_kernel(const uint16
                 ((uint32_t)ops[((4 + r) * 64 + lane) * 8 + 2 * q + 1] << 16);
     }
   f32x16 acc[4];
+  f32x4 acc16[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 4; ++c) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc16[c][r] = 0.0f;
+  }
   i32x4 rs;
   {
     const uint64_t base = (uint64_t)src;
@@ -300,9 +306,14 @@ __global__ __launch_bounds__(NWV * 64) void probe_copy_issue_kernel(const uint16
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int m = 0; m < RM; ++m) {
-      acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[m & 3]),
-                                                           __builtin_bit_cast(bf16x8, b[(m >> 2) & 3]), acc[m & 3], 0,
-                                                           0, 0);
+      if constexpr (S16)
+        acc16[m & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m & 3]),
+                                                               __builtin_bit_cast(bf16x8, b[(m >> 2) & 3]),
+                                                               acc16[m & 3], 0, 0, 0);
+      else
+        acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[m & 3]),
+                                                             __builtin_bit_cast(bf16x8, b[(m >> 2) & 3]), acc[m & 3],
+                                                             0, 0, 0);
       if (NB > 0 && (m % SP) == SP - 1) {
 #pragma unroll
         for (int q = 0; q < BURST; ++q) {
@@ -323,9 +334,12 @@ __global__ __launch_bounds__(NWV * 64) void probe_copy_issue_kernel(const uint16
   const uint64_t t1 = __builtin_amdgcn_s_memtime();
   float s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 4; ++c) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += acc[c][r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s += acc16[c][r];
+  }
   sink[blockIdx.x * 512 + tid] = s + (float)lds[tid];
   if (tid == 0) ticks[blockIdx.x] = t1 - t0;
 }
@@ -447,18 +461,20 @@ extern "C" int tcg_probe_copy_issue(int pattern, int workgroups, int iters, cons
     return GEMM_E_ARG;
   const dim3 g((uint32_t)workgroups);
   const hipStream_t s = (hipStream_t)stream;
-#define TCG_COPY_CASE(P, NWV, NB, BURST)                                                                  \
+#define TCG_COPY_CASE(P, NWV, NB, BURST, S16)                                                             \
   case P:                                                                                                 \
-    hipLaunchKernelGGL((probe_copy_issue_kernel<NWV, NB, BURST>), g, dim3(NWV * 64), 0, s, operands_dev, src_dev, \
+    hipLaunchKernelGGL((probe_copy_issue_kernel<NWV, NB, BURST, S16>), g, dim3(NWV * 64), 0, s, operands_dev, src_dev, \
                        iters, sink_dev, ticks_dev);                                                       \
     break;
   switch (pattern) {
-    TCG_COPY_CASE(TCG_PROBE_COPY_4W_NONE, 4, 0, 0)
-    TCG_COPY_CASE(TCG_PROBE_COPY_4W_8X1, 4, 8, 1)
-    TCG_COPY_CASE(TCG_PROBE_COPY_4W_2X4, 4, 2, 4)
-    TCG_COPY_CASE(TCG_PROBE_COPY_8W_NONE, 8, 0, 0)
-    TCG_COPY_CASE(TCG_PROBE_COPY_8W_4X1, 8, 4, 1)
-    TCG_COPY_CASE(TCG_PROBE_COPY_8W_8X1, 8, 8, 1)
+    TCG_COPY_CASE(TCG_PROBE_COPY_4W_NONE, 4, 0, 0, false)
+    TCG_COPY_CASE(TCG_PROBE_COPY_4W_8X1, 4, 8, 1, false)
+    TCG_COPY_CASE(TCG_PROBE_COPY_4W_2X4, 4, 2, 4, false)
+    TCG_COPY_CASE(TCG_PROBE_COPY_8W_NONE, 8, 0, 0, false)
+    TCG_COPY_CASE(TCG_PROBE_COPY_8W_4X1, 8, 4, 1, false)
+    TCG_COPY_CASE(TCG_PROBE_COPY_8W_8X1, 8, 8, 1, false)
+    TCG_COPY_CASE(TCG_PROBE_COPY_4W_NONE_16X16, 4, 0, 0, true)
+    TCG_COPY_CASE(TCG_PROBE_COPY_4W_8X1_16X16, 4, 8, 1, true)
     default:
       return GEMM_E_ARG;
   }

@@ -164,10 +164,15 @@ def mfma_rate(kind: int, workgroups: int, iters: int, operands: torch.Tensor, si
     return workgroups * 4 * iters * 64 * per_mfma
 
 
-COPY_PATTERNS = {0: ("4 waves, no copies", 4), 1: ("4 waves, 8 copies, 1 per 4 MFMAs", 4),
-                 2: ("4 waves, 8 copies, 2 bursts of 4", 4), 3: ("8 waves, no copies", 8),
-                 4: ("8 waves, 4 copies each (same per SIMD as 1)", 8),
-                 5: ("8 waves, 8 copies each (twice 1 per SIMD)", 8)}
+# pattern: (name, waves per workgroup, MFMAs per round per wave)
+COPY_PATTERNS = {0: ("4 waves, no copies", 4, 32), 1: ("4 waves, 8 copies, 1 per 4 MFMAs", 4, 32),
+                 2: ("4 waves, 8 copies, 2 bursts of 4", 4, 32), 3: ("8 waves, no copies", 8, 32),
+                 4: ("8 waves, 4 copies each (same per SIMD as 1)", 8, 32),
+                 5: ("8 waves, 8 copies each (twice 1 per SIMD)", 8, 32),
+                 6: ("4 waves, no copies, 16x16x32 MFMAs", 4, 64),
+                 7: ("4 waves, 8 copies, 1 per 8 16x16x32 MFMAs (same per flop as 1)", 4, 64)}
+# flops of one MFMA of each pattern's shape
+COPY_PATTERN_MFMA_FLOPS = {p: (16384 if rm == 64 else 32768) for p, (_, _, rm) in COPY_PATTERNS.items()}
 
 
 def copy_issue(pattern: int, workgroups: int, iters: int, operands: torch.Tensor, src: torch.Tensor,
@@ -182,4 +187,5 @@ def copy_issue(pattern: int, workgroups: int, iters: int, operands: torch.Tensor
     f = _fn("tcg_probe_copy_issue", [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp])
     _check(f(pattern, workgroups, iters, operands.data_ptr(), src.data_ptr(), sink.data_ptr(),
              ticks.data_ptr(), s), "tcg_probe_copy_issue")
-    return iters * 32 * (COPY_PATTERNS[pattern][1] // 4)
+    _, waves, per_round = COPY_PATTERNS[pattern]
+    return iters * per_round * (waves // 4)

@@ -288,5 +288,7 @@ def test_copy_issue_probe_runs_every_pattern(probe):
     print(f"cycles per MFMA per SIMD: {got}", flush=True)
     assert 31.5 <= got[0] <= 40 and 31.5 <= got[3] <= 40
     assert got[1] >= got[0] * 0.98 and got[4] >= got[3] * 0.98
+    # the 16x16x32 shape: half the cycles of an MFMA at the peak rate
+    assert 15.5 <= got[6] <= 24 and got[7] >= got[6] * 0.98
     with pytest.raises(RuntimeError):
         probe.copy_issue(99, wg, 1, ops, src, sink, ticks)
